@@ -1,0 +1,201 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) quantized mixture-of-experts FFN layer.
+ *
+ * The layer computes, for T tokens x[t] (bf16, hidden size H):
+ *   z[t, e]  = Wr[e, :] . x[t] + b[e]                router logits, fp32
+ *   S_t      = the k largest z[t, :]                 top-k, ties to the lower expert id
+ *   w[t, j]  = softmax over the k selected logits    routing weights
+ *   y[t]     = sum_{e in S_t} w[t, e] * W_d[e] (silu(W_g[e] x[t]) * (W_u[e] x[t]))
+ * with W_g, W_u, W_d held per expert in one of three precision tiers (bf16,
+ * int8 per-channel, int4 group-128), activations in bf16 and all accumulation
+ * in fp32.
+ *
+ * Sources of the operations (web pages):
+ *   "Every Expert Counts: ExactMoE for Memory-Efficient W4A16 Inference"
+ *     §3.1  router equation z = W_r h and S = TopK(z, k); the router stays BF16;
+ *           W_g, W_u, W_d replaced by quantized forms whose dequantized values
+ *           define the operation;
+ *     §3.2  symmetric group-128 int4 quantizer s = max|W|/7,
+ *           q = clip(round(W/s), -8, 7), and the memory equation
+ *           P (4/8 + 16/(128*8)) bytes;
+ *     §3.3  packed gate/up weights, packed down weights and their FP16 scales
+ *           stored once in the kernel's own format;
+ *     §3.4  tokens grouped by expert, one fused gate/up grouped GEMM and one
+ *           down grouped GEMM per call, a global expert map, router weights
+ *           not renormalized, output = sum of the experts' contributions.
+ *   "Dynamic Expert Quantization for Scalable Mixture-of-Experts Inference"
+ *     (abstract): hot experts at higher precision, low-precision fallback for
+ *     the rest, switched through stable expert handles so a forward pass always
+ *     runs on a fully materialized expert version.
+ *   MxMoE (abstract): GEMMs of different precisions executed together in one
+ *     grouped kernel.
+ *
+ * Conventions for every entry point:
+ *   - Return value: MOE_OK (0) or a positive moe_status code.  On error a
+ *     message is kept per thread and returned by moe_last_error().
+ *   - All argument validation happens on the host before any HIP call; a
+ *     rejected call enqueues nothing.
+ *   - "device" pointers are HIP device memory (hipMalloc / torch CUDA tensors);
+ *     "host" pointers are ordinary CPU memory.  The caller owns every buffer it
+ *     passes and keeps it alive until the stream work that uses it completes.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     moe_route and moe_layer_forward only enqueue work: they never allocate,
+ *     never synchronize and never copy data to the host.  Device faults show up
+ *     at the caller's next synchronization.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *   - Results are deterministic: the same inputs give the same bytes.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,  /* null or misaligned pointer, bad enum value            */
+  MOE_ESHAPE = 2,  /* dimension constraint violated                        */
+  MOE_ERANGE = 3,  /* non-finite weight or fp16 scale overflow when packing  */
+  MOE_ENOSPC = 4,  /* destination or workspace too small                    */
+  MOE_EHIP = 5     /* HIP runtime or launch error (text in moe_last_error)  */
+} moe_status;
+
+/* Precision tier of one expert. */
+typedef enum moe_tier {
+  MOE_TIER_BF16 = 0,  /* bf16 weights as given                               */
+  MOE_TIER_INT8 = 1,  /* symmetric int8, one fp16 scale per output row         */
+  MOE_TIER_INT4 = 2   /* symmetric int4, one fp16 scale per (row, 128 inputs)  */
+} moe_tier;
+
+/* Row order of a packed matrix. */
+typedef enum moe_layout {
+  MOE_LAYOUT_PLAIN = 0,   /* down projection W_d [H, I]                        */
+  MOE_LAYOUT_GATE_UP = 1  /* fused [W_g; W_u] of shape [2I, H], gate rows first;
+                             packed with gate and up rows interleaved in blocks
+                             of 32 so one tile holds matching gate/up columns  */
+} moe_layout;
+
+typedef enum moe_dtype { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 } moe_dtype;
+
+/* One expert's current materialized version (the DynaExq stable handle).
+ * w13 is the packed MOE_LAYOUT_GATE_UP blob of [W_g; W_u] ([2I, H]);
+ * w2 is the packed MOE_LAYOUT_PLAIN blob of W_d ([H, I]); both device pointers,
+ * 256-byte aligned, in the tier given, owned by the caller and kept alive while
+ * any forward that can see this handle is in flight.  flags must be 0. */
+typedef struct moe_expert_handle {
+  int32_t tier;
+  int32_t flags;
+  const void* w13;
+  const void* w2;
+} moe_expert_handle;
+
+/* Layer geometry.  Constraints: hidden % 256 == 0, inter % 128 == 0,
+ * 1 <= n_experts <= 1024, 1 <= top_k <= min(n_experts, 16). */
+typedef struct moe_layer_desc {
+  int32_t hidden;     /* H */
+  int32_t inter;      /* I (per-expert intermediate size) */
+  int32_t n_experts;  /* E */
+  int32_t top_k;      /* k */
+} moe_layer_desc;
+
+typedef struct moe_layer_s* moe_layer_t;
+
+/* Bytes of a packed blob for an [n_out, k_in] matrix in the given tier,
+ * rounded up to a multiple of 256.  int4: n*k/2 + 2*n*k/128 (exactly the
+ * ExactMoE §3.2 memory equation); int8: n*k + 2*n; bf16: 2*n*k.
+ * Returns 0 for a bad tier or a shape the layout cannot hold
+ * (k_in % 128 != 0 or n_out % 16 != 0). */
+size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in);
+
+/* Quantize (ExactMoE §3.2; int8: the same rule per row with range +-127) and
+ * pack one matrix into the kernel's layout, on the GPU.
+ *   w_bf16    device, [n_out, k_in] bf16 master weight (PyTorch Linear layout).
+ *   layout    MOE_LAYOUT_PLAIN or MOE_LAYOUT_GATE_UP (then n_out = 2I with
+ *             I % 32 == 0 and rows 0..I-1 the gate, I..2I-1 the up projection).
+ *   dst       device, 256-byte aligned, dst_bytes >= moe_packed_size(...).
+ * Scales are fp16 (nearest-even of the fp32 quotient max/7 or max/127); codes
+ * use round-half-to-even of w / scale.  This is set-up work, not the hot path:
+ * it synchronizes the stream and returns MOE_ERANGE if a weight is non-finite
+ * or a scale overflows fp16 (dst is then unspecified).  It allocates and frees
+ * one 4-byte device flag per call. */
+int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_out,
+                      int64_t k_in, void* dst, size_t dst_bytes, void* stream);
+
+/* Create a layer.  table: host array of n_experts handles, copied into a
+ * library-owned device table on `stream` (stream-ordered).  The layer object
+ * is owned by the caller until moe_layer_destroy. */
+int moe_layer_create(const moe_layer_desc* desc, const moe_expert_handle* table,
+                     void* stream, moe_layer_t* out);
+
+/* Replace handles [first, first+count) (DynaExq-style promotion/demotion).
+ * The update is enqueued on `stream`: forwards enqueued on that stream later
+ * see the new versions, earlier ones the old.  The host array may be reused as
+ * soon as the call returns (handles travel as kernel arguments). */
+int moe_layer_set_experts(moe_layer_t layer, int32_t first, int32_t count,
+                          const moe_expert_handle* handles, void* stream);
+
+/* Free the layer's device table.  The caller must have synchronized every
+ * stream that has work using the layer. */
+int moe_layer_destroy(moe_layer_t layer);
+
+/* Bytes of device workspace a route or forward call with T tokens needs.
+ * The workspace is scratch: no state is kept in it between calls. */
+size_t moe_workspace_size(moe_layer_t layer, int32_t T);
+
+/* Routing only (ExactMoE §3.1 and §3.4 grouping).  All pointers device.
+ *   x [T, H] bf16;  wr [E, H] bf16;  bias [E] fp32 or NULL.
+ *   topk_ids [T, k] int32: the k selected experts of each token, ascending.
+ *   topk_w   [T, k] fp32: their softmax weights (aligned with topk_ids).
+ *   logits   [T, E] fp32 or NULL: z, summed in the fixed order
+ *            chain j = sum over slabs i, then r = 0..7, of x[256i+8j+r]*wr[..]
+ *            (32 chains), folded pairwise (j += j+s for s = 16,8,4,2,1), plus b.
+ *   expert_offsets [E+1] int32: exclusive prefix sum of routes per expert.
+ *   sorted_routes  [T*k] int32: route ids r = t*k + j grouped by expert, each
+ *                  group in increasing token order.
+ *   route_pos      [T*k] int32: position of route r in sorted_routes.
+ *   ws: device workspace of ws_bytes >= moe_workspace_size(layer, T).
+ * T may be 0 (then only expert_offsets is written, all zero). */
+int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
+              const float* bias, int32_t T, int32_t* topk_ids, float* topk_w,
+              float* logits, int32_t* expert_offsets, int32_t* sorted_routes,
+              int32_t* route_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: route, group, gate/up GEMM + SwiGLU, down GEMM, combine.
+ *   x [T, H] bf16, wr [E, H] bf16, bias [E] fp32 or NULL (device).
+ *   y [T, H] device, bf16 (y_dtype MOE_DTYPE_BF16) or fp32 (MOE_DTYPE_F32);
+ *     the bf16 output is the round-to-nearest-even of the fp32 one.
+ *   ws: device workspace of ws_bytes >= moe_workspace_size(layer, T), 256-byte
+ *     aligned.  x and y must be 16-byte aligned.
+ * T may be 0 (nothing is enqueued).  Calls that share a workspace must be
+ * ordered on one stream. */
+int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
+                      const float* bias, int32_t T, void* y, int y_dtype, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Optional timing hook: when events (hipEvent_t passed as void*) are set, each
+ * forward records events[i] before stage i and events[n-1] after the last
+ * stage, on the forward's stream.  Stages: 0 route logits, 1 top-k,
+ * 2 grouping, 3 gate/up GEMM + SwiGLU, 4 down GEMM, 5 combine; n must be 7.
+ * Pass n = 0 to turn it off.  The events are owned by the caller. */
+int moe_layer_set_stage_events(moe_layer_t layer, void* const* events, int32_t n);
+
+/* Text of a status code (static storage). */
+const char* moe_strerror(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

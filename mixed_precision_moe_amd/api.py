@@ -1,0 +1,188 @@
+"""Python binding of the MoE layer library: argument marshalling only.
+
+Every function maps torch tensors (device memory) and the current HIP stream
+to the C ABI of include/moe.h and returns.  No arithmetic of the layer runs in
+Python; torch provides allocation and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUT_GATE_UP, LAYOUT_PLAIN, TIER_BF16, TIER_INT4,
+                   TIER_INT8, ExpertHandle, LayerDesc, MoeError, check)
+
+__all__ = [
+    "TIER_BF16", "TIER_INT8", "TIER_INT4", "LAYOUT_PLAIN", "LAYOUT_GATE_UP", "MoeError",
+    "packed_size", "quantize_pack", "pack_expert", "Layer",
+]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _require_cuda(t: torch.Tensor, name: str, dtypes: Sequence[torch.dtype]) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def packed_size(tier: int, n_out: int, k_in: int) -> int:
+    return int(_lib.load().moe_packed_size(int(tier), int(n_out), int(k_in)))
+
+
+def quantize_pack(w: torch.Tensor, tier: int, layout: int = LAYOUT_PLAIN,
+                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Quantize and pack one [n_out, k_in] bf16 matrix on the GPU -> uint8 blob."""
+    _require_cuda(w, "w", _BF16)
+    n, k = w.shape
+    size = packed_size(tier, n, k)
+    if size == 0:
+        raise MoeError(_lib.MOE_ESHAPE, "quantize_pack", f"unsupported shape {tuple(w.shape)}")
+    if out is None:
+        out = torch.empty(size, dtype=torch.uint8, device=w.device)
+    check(_lib.load().moe_quantize_pack(int(tier), int(layout), w.data_ptr(), n, k,
+                                        out.data_ptr(), out.numel(), _stream(stream)),
+          "moe_quantize_pack")
+    return out
+
+
+def pack_expert(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, tier: int,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(w13 blob, w2 blob) of one expert from its bf16 [I,H], [I,H], [H,I] weights."""
+    w13 = torch.cat([w_gate, w_up], dim=0).contiguous()
+    return (quantize_pack(w13, tier, LAYOUT_GATE_UP, stream=stream),
+            quantize_pack(w_down.contiguous(), tier, LAYOUT_PLAIN, stream=stream))
+
+
+class Layer:
+    """A quantized MoE layer: geometry plus the device table of expert handles.
+
+    handles: per expert (tier, w13_blob, w2_blob) with blobs from pack_expert.
+    The Layer keeps references to the blobs so they outlive its use.
+    """
+
+    def __init__(self, hidden: int, inter: int, n_experts: int, top_k: int,
+                 handles: Sequence[Tuple[int, torch.Tensor, torch.Tensor]], stream=None):
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+        self._lib = _lib.load()
+        self._blobs: List[Tuple[torch.Tensor, torch.Tensor]] = [(h[1], h[2]) for h in handles]
+        arr = self._handle_array(handles)
+        desc = LayerDesc(hidden, inter, n_experts, top_k)
+        out = ctypes.c_void_p()
+        check(self._lib.moe_layer_create(ctypes.byref(desc), arr, _stream(stream),
+                                         ctypes.byref(out)), "moe_layer_create")
+        self._h = out
+        self._events = None
+        self._ws: Dict[Tuple[int, int], torch.Tensor] = {}
+
+    @staticmethod
+    def _handle_array(handles):
+        arr = (ExpertHandle * max(1, len(handles)))()
+        for i, (tier, w13, w2) in enumerate(handles):
+            arr[i] = ExpertHandle(int(tier), 0, w13.data_ptr(), w2.data_ptr())
+        return arr
+
+    def set_experts(self, first: int, handles, stream=None) -> None:
+        """Stream-ordered replacement of handles [first, first+len(handles))."""
+        arr = self._handle_array(handles)
+        check(self._lib.moe_layer_set_experts(self._h, int(first), len(handles), arr,
+                                              _stream(stream)), "moe_layer_set_experts")
+        for i, h in enumerate(handles):
+            self._blobs[first + i] = (h[1], h[2])
+
+    def workspace_size(self, T: int) -> int:
+        return int(self._lib.moe_workspace_size(self._h, int(T)))
+
+    def workspace(self, T: int, device) -> torch.Tensor:
+        """A cached workspace tensor large enough for T tokens (allocated by torch)."""
+        dev = torch.device(device)
+        key = (dev.index or 0, int(T))
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = torch.empty(max(256, self.workspace_size(T)), dtype=torch.uint8, device=dev)
+            self._ws[key] = ws
+        return ws
+
+    def route(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+        _require_cuda(x, "x", _BF16)
+        _require_cuda(wr, "wr", _BF16)
+        if bias is not None:
+            _require_cuda(bias, "bias", (torch.float32,))
+        T = x.shape[0]
+        dev = x.device
+        k, E = self.top_k, self.n_experts
+        out = dict(
+            ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+            weights=torch.empty((T, k), dtype=torch.float32, device=dev),
+            logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+            offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            sorted_routes=torch.empty(T * k, dtype=torch.int32, device=dev),
+            route_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+        )
+        ws = self.workspace(T, dev) if workspace is None else workspace
+        check(self._lib.moe_route(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), T,
+                                  out["ids"].data_ptr(), out["weights"].data_ptr(),
+                                  out["logits"].data_ptr(), out["offsets"].data_ptr(),
+                                  out["sorted_routes"].data_ptr(), out["route_pos"].data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream(stream)), "moe_route")
+        return out
+
+    def forward(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.float32, y: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        _require_cuda(x, "x", _BF16)
+        _require_cuda(wr, "wr", _BF16)
+        if bias is not None:
+            _require_cuda(bias, "bias", (torch.float32,))
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.hidden), dtype=out_dtype, device=x.device)
+        _require_cuda(y, "y", (torch.float32, torch.bfloat16))
+        yd = DTYPE_F32 if y.dtype == torch.float32 else DTYPE_BF16
+        ws = self.workspace(T, x.device) if workspace is None else workspace
+        check(self._lib.moe_layer_forward(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), T,
+                                          y.data_ptr(), yd, ws.data_ptr(), ws.numel(),
+                                          _stream(stream)), "moe_layer_forward")
+        return y
+
+    def set_stage_events(self, events: Optional[Sequence["torch.cuda.Event"]]) -> None:
+        """Per-stage timing events (7 torch.cuda.Event with timing), or None."""
+        if not events:
+            check(self._lib.moe_layer_set_stage_events(self._h, None, 0), "set_stage_events")
+            self._events = None
+            return
+        for ev in events:
+            if ev.cuda_event == 0:      # torch creates the event lazily
+                ev.record()
+        arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
+        check(self._lib.moe_layer_set_stage_events(self._h, arr, len(events)), "set_stage_events")
+        self._events = list(events)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            check(self._lib.moe_layer_destroy(self._h), "moe_layer_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

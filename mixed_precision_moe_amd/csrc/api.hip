@@ -1,0 +1,396 @@
+// api.hip -- the C ABI: validation, layer object, workspace plan, launch order.
+//
+// The launch order of one forward follows the call stack of "Every Expert
+// Counts: ExactMoE ..." §3.4 with every expert resident (one wave holding all
+// experts): router -> top-k -> group tokens by expert -> one gate/up grouped
+// GEMM (+SwiGLU) -> one down grouped GEMM (x routing weight) -> sum of the
+// experts' contributions.  Nothing here allocates, synchronizes or copies to
+// the host on that path.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return set_error(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
+  WsPlan w{};
+  const size_t R = (size_t)T * L.k;
+  w.max_tiles13 = (int)(R / gp.bm13) + (int)(R < (size_t)L.E ? R : (size_t)L.E);
+  w.max_tiles2 = (int)(R / gp.bm2) + (int)(R < (size_t)L.E ? R : (size_t)L.E);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = round_up(o + bytes, kBlobAlign);
+    return at;
+  };
+  w.logits = take(sizeof(float) * T * (size_t)L.E);
+  w.ids = take(sizeof(int32_t) * R);
+  w.weights = take(sizeof(float) * R);
+  w.offsets = take(sizeof(int32_t) * (L.E + 1));
+  w.sorted = take(sizeof(int32_t) * R);
+  w.pos = take(sizeof(int32_t) * R);
+  w.tiles13 = take(sizeof(TileEntry) * (size_t)(w.max_tiles13 > 0 ? w.max_tiles13 : 1));
+  w.ntiles13 = take(sizeof(int32_t));
+  w.tiles2 = take(sizeof(TileEntry) * (size_t)(w.max_tiles2 > 0 ? w.max_tiles2 : 1));
+  w.ntiles2 = take(sizeof(int32_t));
+  w.r13 = take(sizeof(float) * T * (size_t)(L.H / kGroup));
+  w.act = take(sizeof(uint16_t) * R * L.I);
+  w.r2 = take(sizeof(float) * R * (L.I / kGroup));
+  w.rows = take(sizeof(float) * R * L.H);
+  w.total = o;
+  return w;
+}
+
+namespace {
+
+constexpr int kHandlesPerLaunch = 64;
+struct HandleBatch {
+  moe_expert_handle h[kHandlesPerLaunch];
+};
+
+__global__ void set_handles_kernel(DevHandle* table, int first, int count, HandleBatch b) {
+  const int i = threadIdx.x;
+  if (i < count) {
+    DevHandle d;
+    d.tier = b.h[i].tier;
+    d.flags = b.h[i].flags;
+    d.w13 = reinterpret_cast<const uint8_t*>(b.h[i].w13);
+    d.w2 = reinterpret_cast<const uint8_t*>(b.h[i].w2);
+    table[first + i] = d;
+  }
+}
+
+int validate_handles(const moe_expert_handle* h, int count) {
+  for (int i = 0; i < count; ++i) {
+    if (h[i].tier < MOE_TIER_BF16 || h[i].tier > MOE_TIER_INT4)
+      return set_error(MOE_EINVAL, "handle %d: bad tier %d", i, h[i].tier);
+    if (h[i].flags != 0) return set_error(MOE_EINVAL, "handle %d: flags must be 0", i);
+    if (!h[i].w13 || !h[i].w2) return set_error(MOE_EINVAL, "handle %d: null weight pointer", i);
+    if (!aligned(h[i].w13, kBlobAlign) || !aligned(h[i].w2, kBlobAlign))
+      return set_error(MOE_EINVAL, "handle %d: weight blobs must be 256-byte aligned", i);
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+hipError_t launch_set_handles(DevHandle* table, int first, int count,
+                              const moe_expert_handle* h, hipStream_t s) {
+  for (int done = 0; done < count; done += kHandlesPerLaunch) {
+    const int n = count - done < kHandlesPerLaunch ? count - done : kHandlesPerLaunch;
+    HandleBatch b;
+    memset(&b, 0, sizeof b);
+    memcpy(b.h, h + done, sizeof(moe_expert_handle) * n);
+    hipLaunchKernelGGL(set_handles_kernel, dim3(1), dim3(kHandlesPerLaunch), 0, s, table,
+                       first + done, n, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ESHAPE: return "unsupported shape";
+    case MOE_ERANGE: return "value out of range";
+    case MOE_ENOSPC: return "buffer too small";
+    case MOE_EHIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in) {
+  if (n_out <= 0 || k_in <= 0 || k_in % kGroup || n_out % 16) return 0;
+  size_t bytes;
+  switch (tier) {
+    case MOE_TIER_INT4: bytes = (size_t)n_out * k_in / 2 + (size_t)n_out * (k_in / kGroup) * 2; break;
+    case MOE_TIER_INT8: bytes = (size_t)n_out * k_in + 2 * (size_t)n_out; break;
+    case MOE_TIER_BF16: bytes = 2 * (size_t)n_out * k_in; break;
+    default: return 0;
+  }
+  return round_up(bytes, kBlobAlign);
+}
+
+int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_out, int64_t k_in,
+                      void* dst, size_t dst_bytes, void* stream) {
+  g_err[0] = 0;
+  if (tier < MOE_TIER_BF16 || tier > MOE_TIER_INT4)
+    return set_error(MOE_EINVAL, "bad tier %d", tier);
+  if (layout != MOE_LAYOUT_PLAIN && layout != MOE_LAYOUT_GATE_UP)
+    return set_error(MOE_EINVAL, "bad layout %d", layout);
+  if (!w_bf16 || !dst) return set_error(MOE_EINVAL, "null pointer");
+  if (!aligned(dst, kBlobAlign)) return set_error(MOE_EINVAL, "dst must be 256-byte aligned");
+  if (!aligned(w_bf16, 16)) return set_error(MOE_EINVAL, "weights must be 16-byte aligned");
+  if (n_out <= 0 || k_in <= 0 || k_in % kGroup || n_out % 16 || n_out > (1 << 30) ||
+      k_in > (1 << 30))
+    return set_error(MOE_ESHAPE, "need k_in %% 128 == 0 and n_out %% 16 == 0 (got %lld x %lld)",
+                     (long long)n_out, (long long)k_in);
+  if (layout == MOE_LAYOUT_GATE_UP && n_out % 64)
+    return set_error(MOE_ESHAPE, "gate/up layout needs n_out = 2I with I %% 32 == 0");
+  const size_t need = moe_packed_size(tier, n_out, k_in);
+  if (dst_bytes < need)
+    return set_error(MOE_ENOSPC, "dst has %zu bytes, %zu needed", dst_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int* flag = nullptr;
+  int rc = check_hip(hipMalloc(&flag, sizeof(int)), "hipMalloc(flag)");
+  if (rc) return rc;
+  int host_flag = 0;
+  size_t payload;
+  switch (tier) {
+    case MOE_TIER_INT4: payload = (size_t)n_out * k_in / 2 + (size_t)n_out * (k_in / kGroup) * 2; break;
+    case MOE_TIER_INT8: payload = (size_t)n_out * k_in + 2 * (size_t)n_out; break;
+    default: payload = 2 * (size_t)n_out * k_in; break;
+  }
+  if (!rc) rc = check_hip(hipMemsetAsync(flag, 0, sizeof(int), s), "hipMemsetAsync(flag)");
+  if (!rc && need > payload)
+    rc = check_hip(hipMemsetAsync(static_cast<uint8_t*>(dst) + payload, 0, need - payload, s),
+                   "hipMemsetAsync(pad)");
+  if (!rc)
+    rc = check_hip(launch_quantize_pack(tier, layout, w_bf16, n_out, k_in,
+                                        static_cast<uint8_t*>(dst), flag, s),
+                   "quantize_pack launch");
+  if (!rc)
+    rc = check_hip(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, s),
+                   "hipMemcpyAsync(flag)");
+  if (!rc) rc = check_hip(hipStreamSynchronize(s), "hipStreamSynchronize");
+  (void)hipFree(flag);
+  if (!rc && host_flag)
+    rc = set_error(MOE_ERANGE, "non-finite weight or fp16 scale overflow");
+  return rc;
+}
+
+int moe_layer_create(const moe_layer_desc* d, const moe_expert_handle* table, void* stream,
+                     moe_layer_t* out) {
+  g_err[0] = 0;
+  if (!d || !table || !out) return set_error(MOE_EINVAL, "null pointer");
+  *out = nullptr;
+  if (d->hidden <= 0 || d->hidden % 256)
+    return set_error(MOE_ESHAPE, "hidden must be a positive multiple of 256 (got %d)", d->hidden);
+  if (d->inter <= 0 || d->inter % 128)
+    return set_error(MOE_ESHAPE, "inter must be a positive multiple of 128 (got %d)", d->inter);
+  if (d->n_experts < 1 || d->n_experts > kMaxExperts)
+    return set_error(MOE_ESHAPE, "n_experts must be in [1, %d] (got %d)", kMaxExperts, d->n_experts);
+  if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts)
+    return set_error(MOE_ESHAPE, "top_k must be in [1, min(n_experts, %d)] (got %d)", kMaxTopK,
+                     d->top_k);
+  int rc = validate_handles(table, d->n_experts);
+  if (rc) return rc;
+  Layer* L = new (std::nothrow) Layer();
+  if (!L) return set_error(MOE_EINVAL, "out of host memory");
+  L->H = d->hidden;
+  L->I = d->inter;
+  L->E = d->n_experts;
+  L->k = d->top_k;
+  L->n_stage_events = 0;
+  rc = check_hip(hipMalloc(&L->table, sizeof(DevHandle) * L->E), "hipMalloc(table)");
+  if (!rc)
+    rc = check_hip(launch_set_handles(L->table, 0, L->E, table,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                   "set_handles launch");
+  if (rc) {
+    if (L->table) (void)hipFree(L->table);
+    delete L;
+    return rc;
+  }
+  *out = reinterpret_cast<moe_layer_t>(L);
+  return MOE_OK;
+}
+
+int moe_layer_set_experts(moe_layer_t layer, int32_t first, int32_t count,
+                          const moe_expert_handle* handles, void* stream) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L || (!handles && count > 0)) return set_error(MOE_EINVAL, "null pointer");
+  if (first < 0 || count < 0 || first + count > L->E)
+    return set_error(MOE_ESHAPE, "handle range [%d, %d) outside [0, %d)", first, first + count, L->E);
+  int rc = validate_handles(handles, count);
+  if (rc) return rc;
+  return check_hip(launch_set_handles(L->table, first, count, handles,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                   "set_handles launch");
+}
+
+int moe_layer_destroy(moe_layer_t layer) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  const int rc = check_hip(hipFree(L->table), "hipFree(table)");
+  delete L;
+  return rc;
+}
+
+size_t moe_workspace_size(moe_layer_t layer, int32_t T) {
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  if (!L || T < 0) return 0;
+  const GemmPlan gp = plan_gemm(*L, T);
+  return plan_workspace(*L, T, gp).total;
+}
+
+int moe_layer_set_stage_events(moe_layer_t layer, void* const* events, int32_t n) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  if (n != 0 && n != 7) return set_error(MOE_EINVAL, "need 0 or 7 events (got %d)", n);
+  if (n && !events) return set_error(MOE_EINVAL, "null events");
+  for (int i = 0; i < n; ++i) {
+    if (!events[i]) return set_error(MOE_EINVAL, "null event %d", i);
+    L->stage_events[i] = events[i];
+  }
+  L->n_stage_events = n;
+  return MOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_common(const Layer* L, const uint16_t* x, const uint16_t* wr, int32_t T, void* ws,
+                 size_t ws_bytes, WsPlan* plan, GemmPlan* gp) {
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  if (T < 0 || T > (1 << 24)) return set_error(MOE_ESHAPE, "bad token count %d", T);
+  if ((size_t)T * L->k > (size_t)1 << 28) return set_error(MOE_ESHAPE, "too many routes");
+  if (T > 0 && (!x || !wr || !ws)) return set_error(MOE_EINVAL, "null pointer");
+  if (T > 0 && (!aligned(x, 16) || !aligned(wr, 16)))
+    return set_error(MOE_EINVAL, "x and wr must be 16-byte aligned");
+  if (T > 0 && !aligned(ws, kBlobAlign))
+    return set_error(MOE_EINVAL, "workspace must be 256-byte aligned");
+  *gp = plan_gemm(*L, T);
+  *plan = plan_workspace(*L, T, *gp);
+  if (T > 0 && ws_bytes < plan->total)
+    return set_error(MOE_ENOSPC, "workspace has %zu bytes, %zu needed", ws_bytes, plan->total);
+  return MOE_OK;
+}
+
+// Optional per-stage timing events (moe_layer_set_stage_events).
+struct Stages {
+  const Layer* L;
+  hipStream_t s;
+  bool on;
+  void rec(int i) const {
+    if (on && L->n_stage_events == 7)
+      (void)hipEventRecord(reinterpret_cast<hipEvent_t>(L->stage_events[i]), s);
+  }
+};
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, const uint16_t* x,
+                         const uint16_t* wr, const float* bias, int T, float* logits,
+                         int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                         float* r13, void* ws, const Stages& st) {
+  st.rec(0);
+  hipError_t e = launch_router_logits(x, wr, bias, T, L.H, L.E, logits, st.s);
+  if (e != hipSuccess) return e;
+  st.rec(1);
+  e = launch_topk(logits, x, T, L.H, L.E, L.k, ids, w, r13, st.s);
+  if (e != hipSuccess) return e;
+  st.rec(2);
+  return launch_permute(ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
+                        at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
+                        at<int32_t>(ws, p.ntiles2), gp.bm2, st.s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const float* bias,
+              int32_t T, int32_t* topk_ids, float* topk_w, float* logits, int32_t* expert_offsets,
+              int32_t* sorted_routes, int32_t* route_pos, void* ws, size_t ws_bytes,
+              void* stream) {
+  g_err[0] = 0;
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  WsPlan p;
+  GemmPlan gp;
+  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
+  if (rc) return rc;
+  if (!expert_offsets || (T > 0 && (!topk_ids || !topk_w || !sorted_routes || !route_pos)))
+    return set_error(MOE_EINVAL, "null output pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return check_hip(hipMemsetAsync(expert_offsets, 0, sizeof(int32_t) * (L->E + 1), s),
+                     "hipMemsetAsync(offsets)");
+  const Stages st{L, s, false};
+  const hipError_t e = enqueue_route(*L, p, gp, x, wr, bias, T,
+                                     logits ? logits : at<float>(ws, p.logits), topk_ids, topk_w,
+                                     expert_offsets, sorted_routes, route_pos, nullptr, ws, st);
+  return check_hip(e, "route launch");
+}
+
+int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const float* bias,
+                      int32_t T, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  WsPlan p;
+  GemmPlan gp;
+  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
+  if (rc) return rc;
+  if (y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F32)
+    return set_error(MOE_EINVAL, "bad y_dtype %d", y_dtype);
+  if (T == 0) return MOE_OK;
+  if (!y || !aligned(y, 16)) return set_error(MOE_EINVAL, "y must be non-null and 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const Stages st{L, s, true};
+  hipError_t e = enqueue_route(*L, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
+                               at<int32_t>(ws, p.ids), at<float>(ws, p.weights),
+                               at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
+                               at<int32_t>(ws, p.pos), at<float>(ws, p.r13), ws, st);
+  if (e != hipSuccess) return check_hip(e, "route launch");
+  st.rec(3);
+  e = launch_gemm13(*L, gp, T, x, at<int32_t>(ws, p.sorted), at<TileEntry>(ws, p.tiles13),
+                    at<int32_t>(ws, p.ntiles13), p.max_tiles13, at<float>(ws, p.r13),
+                    at<uint16_t>(ws, p.act), at<float>(ws, p.r2), s);
+  if (e != hipSuccess) return check_hip(e, "gate/up GEMM launch");
+  st.rec(4);
+  e = launch_gemm2(*L, gp, T, at<uint16_t>(ws, p.act), at<int32_t>(ws, p.sorted),
+                   at<float>(ws, p.weights), at<TileEntry>(ws, p.tiles2),
+                   at<int32_t>(ws, p.ntiles2), p.max_tiles2, at<float>(ws, p.r2),
+                   at<float>(ws, p.rows), s);
+  if (e != hipSuccess) return check_hip(e, "down GEMM launch");
+  st.rec(5);
+  e = launch_combine(at<float>(ws, p.rows), at<int32_t>(ws, p.pos), T, L->H, L->k, y, y_dtype, s);
+  if (e != hipSuccess) return check_hip(e, "combine launch");
+  st.rec(6);
+  return MOE_OK;
+}
+
+}  // extern "C"

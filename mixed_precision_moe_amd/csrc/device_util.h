@@ -1,0 +1,90 @@
+// device_util.h -- small gfx950 device helpers shared by the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef short bf16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t pair) {
+  return __uint_as_float(pair << 16);
+}
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t pair) {
+  return __uint_as_float(pair & 0xffff0000u);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
+
+// Non-temporal 16-byte load for data read exactly once (weights).
+__device__ __forceinline__ u32x4 load_u32x4_stream(const void* p) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return u32x4{v[0], v[1], v[2], v[3]};
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  v4u t = {v.x, v.y, v.z, v.w};
+  return __builtin_bit_cast(bf16x8_t, t);
+}
+
+// Eight offset-binary int4 codes (nibble value q+8) of one MFMA k-chunk ->
+// eight bf16 operands of value 136 + q, exact.  Nibble j of the word holds
+// element 2j and nibble j+4 holds element 2j+1, so each output register is one
+// shift and one and-or: 0x4300 | u is the bf16 value 128 + u for u < 16.
+__device__ __forceinline__ bf16x8_t int4x8_to_bf16_biased(uint32_t w) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  v4u t;
+  t[0] = (w & 0x000f000fu) | 0x43004300u;
+  t[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
+  t[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
+  t[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8_t, t);
+}
+
+// Four offset-binary int8 codes (byte value q+128) -> two registers of bf16
+// operands of value 128 + q, exact (integers below 256 fit bf16's 8 bits).
+__device__ __forceinline__ uint32_t int8x2_to_bf16_biased(uint32_t w, int shift) {
+  const float f0 = (float)((w >> shift) & 0xffu);
+  const float f1 = (float)((w >> (shift + 8)) & 0xffu);
+  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+}
+
+__device__ __forceinline__ bf16x8_t int8x8_to_bf16_biased(uint32_t w0, uint32_t w1) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  v4u t;
+  t[0] = int8x2_to_bf16_biased(w0, 0);
+  t[1] = int8x2_to_bf16_biased(w0, 16);
+  t[2] = int8x2_to_bf16_biased(w1, 0);
+  t[3] = int8x2_to_bf16_biased(w1, 16);
+  return __builtin_bit_cast(bf16x8_t, t);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+}  // namespace moe

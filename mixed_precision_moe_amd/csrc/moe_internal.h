@@ -1,0 +1,89 @@
+// moe_internal.h -- host-side declarations shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kGroup = 128;        // int4 group size and the k-tile of every layout
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kBlobAlign = 256;
+
+// Device copy of one expert handle (same field order as moe_expert_handle).
+struct DevHandle {
+  int32_t tier;
+  int32_t flags;
+  const uint8_t* w13;
+  const uint8_t* w2;
+};
+static_assert(sizeof(DevHandle) == sizeof(moe_expert_handle), "handle layout");
+
+// One M-tile of a grouped GEMM: rows [row_start, row_start + rows) of the
+// grouped (sorted) route order, all owned by `expert`.
+struct TileEntry {
+  int32_t expert;
+  int32_t row_start;
+  int32_t rows;
+  int32_t pad;
+};
+
+// Tile size choices for one forward, picked on the host from T and the layer.
+struct GemmPlan {
+  int bm13;   // rows per M-tile, gate/up GEMM
+  int bm2;    // rows per M-tile, down GEMM
+  int kind;   // kernel family (see grouped_gemm.hip)
+};
+
+// Byte offsets of the workspace regions for T tokens.
+struct WsPlan {
+  size_t logits, ids, weights, offsets, sorted, pos, tiles13, ntiles13, tiles2, ntiles2;
+  size_t r13, act, r2, rows;
+  size_t total;
+  int max_tiles13, max_tiles2;
+};
+
+struct Layer {
+  int32_t H, I, E, k;
+  DevHandle* table;      // device [E]
+  void* stage_events[7];
+  int32_t n_stage_events;
+};
+
+// error state ---------------------------------------------------------------
+int set_error(int status, const char* fmt, ...);
+int check_hip(hipError_t e, const char* what);
+
+// planning ------------------------------------------------------------------
+GemmPlan plan_gemm(const Layer& L, int T);
+WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp);
+
+// launchers (return hipError_t of the launch) --------------------------------
+hipError_t launch_quantize_pack(int tier, int layout, const uint16_t* w, int64_t n, int64_t k,
+                                uint8_t* dst, int* err_flag, hipStream_t s);
+hipError_t launch_set_handles(DevHandle* table, int first, int count,
+                              const moe_expert_handle* h, hipStream_t s);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                int T, int H, int E, float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int k,
+                       int32_t* ids, float* w, float* r13, hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
+                          int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                          hipStream_t s);
+hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16_t* x,
+                         const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
+                         int max_tiles, const float* r13, uint16_t* act, float* r2,
+                         hipStream_t s);
+hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
+                        const int32_t* sorted, const float* topk_w, const TileEntry* tiles,
+                        const int32_t* ntiles, int max_tiles, const float* r2, float* rows,
+                        hipStream_t s);
+hipError_t launch_combine(const float* rows, const int32_t* pos, int T, int H, int k, void* y,
+                          int y_dtype, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,336 @@
+// route.hip -- router logits, top-k + softmax weights, and grouping by expert.
+//
+// "Every Expert Counts: ExactMoE ..." §3.1: z = W_r h, S = TopK(z, k), the
+// router kept in BF16 and unchanged; §3.4 and Fig. 1: tokens are grouped by
+// selected expert before the grouped GEMMs.
+//
+// Logits are fp32 in one fixed order so that the top-k choice is reproducible
+// bit for bit: 32 chains per dot product, chain j summing x[h]*w[h] for
+// h = 256i + 8j + r (slab i outer, r = 0..7 inner) from +0, then the chains
+// folded pairwise (chain j += chain j+s for s = 16, 8, 4, 2, 1), then + bias.
+// Every bf16 x bf16 product is exact in fp32, so fma and mul-then-add agree.
+// On the GPU one chain is one lane of a half-wave: lane j reads the 16-byte
+// chunk at 256i + 8j, so a half-wave reads each 512-byte slab coalesced, and the
+// fold is a shuffle tree.
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// Block: 8 half-waves (256 threads) arranged 2 (token groups) x 4 (expert
+// groups).  Each half-wave owns TT tokens x TE experts; block tile is
+// (2*TT) tokens x (4*TE) experts.
+template <int TT, int TE>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            int T, int H, int E,
+                                                            float* __restrict__ logits) {
+  const int j = threadIdx.x & 31;           // chain index
+  const int hw = threadIdx.x >> 5;          // half-wave 0..7
+  const int t0 = blockIdx.x * (2 * TT) + (hw >> 2) * TT;
+  const int e0 = blockIdx.y * (4 * TE) + (hw & 3) * TE;
+  const uint16_t* xp[TT];
+  const uint16_t* wp[TE];
+#pragma unroll
+  for (int a = 0; a < TT; ++a) xp[a] = x + (size_t)min(t0 + a, T - 1) * H + 8 * j;
+#pragma unroll
+  for (int b = 0; b < TE; ++b) wp[b] = wr + (size_t)min(e0 + b, E - 1) * H + 8 * j;
+  float acc[TT][TE];
+#pragma unroll
+  for (int a = 0; a < TT; ++a)
+#pragma unroll
+    for (int b = 0; b < TE; ++b) acc[a][b] = 0.0f;
+
+  for (int base = 0; base < H; base += 256) {
+    u32x4 xv[TT], wv[TE];
+#pragma unroll
+    for (int a = 0; a < TT; ++a) xv[a] = load_u32x4(xp[a] + base);
+#pragma unroll
+    for (int b = 0; b < TE; ++b) wv[b] = load_u32x4(wp[b] + base);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      float xf[TT], wf[TE];
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        const uint32_t d = (&xv[a].x)[r >> 1];
+        xf[a] = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
+      }
+#pragma unroll
+      for (int b = 0; b < TE; ++b) {
+        const uint32_t d = (&wv[b].x)[r >> 1];
+        wf[b] = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
+      }
+#pragma unroll
+      for (int a = 0; a < TT; ++a)
+#pragma unroll
+        for (int b = 0; b < TE; ++b) acc[a][b] = __builtin_fmaf(xf[a], wf[b], acc[a][b]);
+    }
+  }
+  // fold the 32 chains: chain j += chain j+s, s = 16 .. 1
+#pragma unroll
+  for (int s = 16; s >= 1; s >>= 1) {
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int b = 0; b < TE; ++b) {
+        const float other = __shfl_down(acc[a][b], s, 32);
+        acc[a][b] = acc[a][b] + other;
+      }
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int b = 0; b < TE; ++b) {
+        const int t = t0 + a, e = e0 + b;
+        if (t < T && e < E) {
+          const float bb = bias ? bias[e] : 0.0f;
+          logits[(size_t)t * E + e] = acc[a][b] + bb;
+        }
+      }
+  }
+}
+
+// better(a, b): larger logit, or equal logit and lower expert id.
+__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
+  return va > vb || (va == vb && ea < eb);
+}
+
+// One wave per token: select the k largest logits (ties -> lower id), softmax
+// over them, store ids ascending with their weights.  Also the per-group sums
+// of the token's activations, R13[t][g] = sum_{h in group g} x[t][h] (used by
+// the GEMM to remove the offset of its biased weight operands).
+constexpr int kMaxPerLane = kMaxExperts / 64;
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   const uint16_t* __restrict__ x, int T, int H,
+                                                   int E, int k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ weights,
+                                                   float* __restrict__ r13) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* z = logits + (size_t)t * E;
+  float v[kMaxPerLane];
+  const int per = (E + 63) / 64;
+#pragma unroll
+  for (int m = 0; m < kMaxPerLane; ++m) {
+    const int e = lane + 64 * m;
+    v[m] = (m < per && e < E) ? z[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  int sel_e[kMaxTopK];
+  float sel_z[kMaxTopK];
+#pragma unroll
+  for (int jj = 0; jj < kMaxTopK; ++jj) {
+    if (jj >= k) break;
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < kMaxPerLane; ++m) {
+      const int e = lane + 64 * m;
+      if (m < per && e < E && !((taken >> m) & 1u) && better(v[m], e, bv, be)) {
+        bv = v[m];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (be >= E) be = jj;   // only reachable with NaN logits (out of domain): stay in bounds
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    sel_e[jj] = be;
+    sel_z[jj] = bv;
+  }
+  // softmax over the selected logits (the first selected one is the largest)
+  if (lane < k) {
+    int my_e = 0;
+    double my_z = 0.0, den = 0.0;
+    const double zmax = (double)sel_z[0];
+#pragma unroll
+    for (int jj = 0; jj < kMaxTopK; ++jj) {
+      if (jj >= k) break;
+      den += exp((double)sel_z[jj] - zmax);
+      if (jj == lane) {
+        my_e = sel_e[jj];
+        my_z = (double)sel_z[jj];
+      }
+    }
+    int rank = 0;
+#pragma unroll
+    for (int jj = 0; jj < kMaxTopK; ++jj) {
+      if (jj >= k) break;
+      rank += sel_e[jj] < my_e;
+    }
+    ids[(size_t)t * k + rank] = my_e;
+    weights[(size_t)t * k + rank] = (float)(exp(my_z - zmax) / den);
+  }
+  if (r13) {
+    // group g, 16 lanes x 8 elements; four groups per pass
+    const uint16_t* xr = x + (size_t)t * H;
+    const int G = H / kGroup;
+    for (int g0 = 0; g0 < G; g0 += 4) {
+      const int g = g0 + (lane >> 4);
+      float s = 0.0f;
+      if (g < G) {
+        const u32x4 q = load_u32x4(xr + kGroup * g + 8 * (lane & 15));
+        s = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
+            (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+      if (g < G && (lane & 15) == 0) r13[(size_t)t * G + g] = s;
+    }
+  }
+}
+
+// Grouping by expert in one workgroup of 1024 threads (16 waves).
+// Tokens are split into 16 contiguous chunks, one per wave.  Per-chunk expert
+// histograms (LDS integer atomics, so the counts are exact) give every wave
+// the base position of its routes inside each expert's segment; a wave then
+// walks its tokens in order, placing the token's k routes (distinct experts)
+// in one step.  The result is the stable order by (expert, token).
+// Finally the M-tile tables of both grouped GEMMs are written.
+__global__ __launch_bounds__(1024) void permute_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
+    int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
+    int32_t* __restrict__ ntiles2, int bm2) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                 // [16][E]
+  int* off = cnt + 16 * E;        // [E+1] exclusive scan of totals
+  int* scan = off + E + 1;        // [1024] scan scratch
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int chunk = (T + 15) / 16;
+  const int tb = min(T, wave * chunk), te = min(T, tb + chunk);
+
+  for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  for (int r = tb * k + lane; r < te * k; r += 64)
+    atomicAdd(&cnt[wave * E + min(max(ids[r], 0), E - 1)], 1);
+  __syncthreads();
+
+  // per expert: prefix over the 16 chunks; total -> off[e]
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+    off[e] = run;
+  }
+  __syncthreads();
+
+  // exclusive scan of totals over experts (E <= 1024: one value per thread)
+  const int mytot = tid < E ? off[tid] : 0;
+  scan[tid] = mytot;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int add = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int excl = scan[tid] - mytot;   // exclusive prefix
+  __syncthreads();
+  if (tid < E) off[tid] = excl;
+  if (tid == 0) off[E] = scan[1023];
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
+
+  // stable scatter: each wave walks its tokens in order
+  for (int t = tb; t < te; ++t) {
+    if (lane < k) {
+      const int r = t * k + lane;
+      const int e = min(max(ids[r], 0), E - 1);
+      const int p = off[e] + cnt[wave * E + e];
+      cnt[wave * E + e] += 1;
+      sorted[p] = r;
+      pos[r] = p;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // M-tile tables: expert e with c_e routes gets ceil(c_e / bm) tiles
+  for (int table = 0; table < 2; ++table) {
+    const int bm = table == 0 ? bm13 : bm2;
+    TileEntry* tiles = table == 0 ? tiles13 : tiles2;
+    int32_t* ntiles = table == 0 ? ntiles13 : ntiles2;
+    const int ce = tid < E ? off[tid + 1] - off[tid] : 0;
+    const int nt = (ce + bm - 1) / bm;
+    scan[tid] = nt;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int add = tid >= d ? scan[tid - d] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int first = scan[tid] - nt;
+    for (int i = 0; i < nt; ++i) {
+      TileEntry te2;
+      te2.expert = tid;
+      te2.row_start = off[tid] + i * bm;
+      te2.rows = min(bm, ce - i * bm);
+      te2.pad = 0;
+      tiles[first + i] = te2;
+    }
+    if (tid == 1023) *ntiles = scan[1023];
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                                int H, int E, float* logits, hipStream_t s) {
+  if (T <= 64) {
+    constexpr int TT = 1, TE = 4;
+    const dim3 grid((T + 2 * TT - 1) / (2 * TT), (E + 4 * TE - 1) / (4 * TE));
+    hipLaunchKernelGGL((router_logits_kernel<TT, TE>), grid, dim3(256), 0, s, x, wr, bias, T, H,
+                       E, logits);
+  } else {
+    constexpr int TT = 4, TE = 4;
+    const dim3 grid((T + 2 * TT - 1) / (2 * TT), (E + 4 * TE - 1) / (4 * TE));
+    hipLaunchKernelGGL((router_logits_kernel<TT, TE>), grid, dim3(256), 0, s, x, wr, bias, T, H,
+                       E, logits);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int k,
+                       int32_t* ids, float* w, float* r13, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, H, E, k, ids,
+                     w, r13);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
+                          int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                          hipStream_t s) {
+  const size_t lds = sizeof(int) * (16 * (size_t)E + E + 1 + 1024);
+  static bool attr_set = false;   // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB)
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(sizeof(int) * (16 * kMaxExperts + kMaxExperts + 1 + 1024)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, ids, T, k, E, offsets, sorted,
+                     pos, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2);
+  return hipGetLastError();
+}
+
+}  // namespace moe
