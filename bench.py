@@ -1,0 +1,294 @@
+"""Benchmark of the quantized MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step is one whole layer forward (routing, grouping, gate/up GEMM + SwiGLU,
+down GEMM, combine) over one batch of synthetic tokens already resident in
+HBM.  The default workload is the Qwen3-30B-A3B-shaped decode layer
+(H 2048, E 128, top-8, I 768, all experts int4 group-128, 32 tokens).  Weight
+sets are rotated across R device copies so consecutive steps do not re-read
+weights from the 256 MB last-level cache.
+
+Prints one JSON line: whole-job tokens/s, the dominant kernel's roofline
+(algorithmic bytes or flops per launch over its measured average duration,
+from HIP events recorded on the forward's stream inside the timed region),
+and the CPU oracle timed on a bounded sample as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import inputs  # noqa: E402
+
+METRIC = "MoE-layer tokens/s; % HBM roofline (decode) and % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+STAGES = ["route_logits", "topk", "grouping", "gemm_gate_up_swiglu", "gemm_down", "combine"]
+KERNEL_SOURCE = os.path.join(ROOT, "mixed_precision_moe_amd", "csrc", "grouped_gemm.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def packed_bytes(tier, n, k):
+    if tier == 2:
+        return n * k // 2 + n * (k // 128) * 2
+    if tier == 1:
+        return n * k + 2 * n
+    return 2 * n * k
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def build_layers(cfg, tiers, R, dev):
+    """R Layer objects over R distinct device copies of the packed experts."""
+    import torch
+    import mixed_precision_moe_amd as mm
+    blobs = []
+    for e in range(cfg.n_experts):
+        wg, wu, wd = inputs.gen_expert(cfg, e)
+        t = [torch.from_numpy(a.view(np.int16)).to(dev) for a in (wg, wu, wd)]
+        blobs.append(mm.pack_expert(*t, int(tiers[e])))
+        del t
+    layers = []
+    for r in range(R):
+        hs = []
+        for e in range(cfg.n_experts):
+            w13, w2 = blobs[e] if r == 0 else (blobs[e][0].clone(), blobs[e][1].clone())
+            hs.append((int(tiers[e]), w13, w2))
+        layers.append(mm.Layer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, hs))
+    torch.cuda.synchronize()
+    return layers
+
+
+def algorithmic(cfg, tiers, ids, T):
+    """Algorithmic bytes and flops of the two grouped GEMMs for this routing."""
+    touched = np.unique(ids)
+    H, I, k = cfg.hidden, cfg.inter, cfg.top_k
+    w13 = sum(packed_bytes(int(tiers[e]), 2 * I, H) for e in touched)
+    w2 = sum(packed_bytes(int(tiers[e]), H, I) for e in touched)
+    b13 = w13 + 2 * T * H + 2 * T * k * I            # weights + x in + activation out
+    b2 = w2 + 2 * T * k * I + 4 * T * k * H          # weights + activation in + rows out
+    f13 = 2.0 * T * k * H * 2 * I
+    f2 = 2.0 * T * k * I * H
+    router = 2 * cfg.n_experts * H
+    return dict(touched=int(touched.size), bytes13=b13, bytes2=b2, flops13=f13, flops2=f2,
+                bytes_layer=w13 + w2 + 4 * T * H + router, flops_layer=f13 + f2)
+
+
+def cpu_baseline(cfg, tiers, x, wr, bias, min_seconds=10.0, max_seconds=30.0):
+    """The oracle forward (dequantize touched experts, route, expert FFNs,
+    combine) timed on this host over the same synthetic batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                   # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    r0 = oracle.route(x, wr, bias, cfg.top_k)
+    touched = np.unique(r0["ids"])
+    pre = {}
+    for e in touched:                                     # quantization is not timed
+        wg, wu, wd = inputs.gen_expert(cfg, int(e))
+        w13 = np.concatenate([wg, wu], axis=0)
+        t = int(tiers[e])
+        pre[int(e)] = (t, oracle.quantize_tier(t, w13), oracle.quantize_tier(t, wd), w13, wd)
+    I = cfg.inter
+
+    def get(e):
+        t, (q13, s13), (q2, s2), w13, wd = pre[e]
+        w13h = oracle.dequantize(t, q13, s13, w13)
+        return oracle.OracleExpert(t, w13h[:I], w13h[I:], oracle.dequantize(t, q2, s2, wd))
+
+    import contextlib
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            r = oracle.route(x, wr, bias, cfg.top_k)
+            oracle.layer_forward(x, r, get)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or el * (reps + 1) / reps > max_seconds:
+                break
+    T = x.shape[0]
+    return {"value": round(T * reps / el, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} full forward(s) of the same {T}-token batch (dequantize "
+                      f"{touched.size} touched experts, route, expert FFNs, combine; "
+                      f"quantization excluded); numpy float64, BLAS pool of {cores} threads",
+            "seconds": round(el, 2)}
+
+
+def stored_traffic(workload_key):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path)).get(workload_key)
+    except (ValueError, OSError):
+        return None
+    if not d or d.get("source_sha") != source_hash():
+        return None
+    return d.get("traffic_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(inputs.CONFIGS))
+    ap.add_argument("--tokens", type=int, default=None, help="token count (default: the config's)")
+    ap.add_argument("--rotate", type=int, default=None, help="weight-set copies (default: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run plain device copies of this many MiB (for scaling HBM "
+                         "counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer is measured on "
+              f"a single MI355X; multi-GPU sharding is described in the design notes, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixed_precision_moe_amd as mm  # noqa: F401
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x 3 (read {n}, write {n} per copy)")
+        return
+    cfg = inputs.get_config(args.config)
+    T = cfg.default_tokens if args.tokens is None else args.tokens
+    tiers = inputs.gen_tiers(cfg)
+    x_np, wr_np, bias_np = inputs.gen_tokens(cfg, T), inputs.gen_router(cfg), inputs.gen_bias(cfg)
+    total_w = sum(packed_bytes(int(tiers[e]), 2 * cfg.inter, cfg.hidden) +
+                  packed_bytes(int(tiers[e]), cfg.hidden, cfg.inter) for e in range(cfg.n_experts))
+    R = args.rotate or max(1, min(16, int(np.ceil(1.0e9 / total_w))))
+    log(f"[bench] {cfg.describe(T)}; weights {total_w / 1e6:.1f} MB x {R} rotating copies")
+    t0 = time.time()
+    layers = build_layers(cfg, tiers, R, dev)
+    log(f"[bench] packed in {time.time() - t0:.1f} s")
+
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev)
+    wr = torch.from_numpy(wr_np.view(np.int16)).to(dev)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
+    ydt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+    y = torch.empty((T, cfg.hidden), dtype=ydt, device=dev)
+    ws = torch.empty(layers[0].workspace_size(T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    fwd = [L.bind_forward(x, wr, bias, y, workspace=ws, stream=stream) for L in layers]
+
+    # routing (for the algorithmic byte/flop counts): outside the timed region
+    route = layers[0].route(x, wr, bias)
+    ids = route["ids"].cpu().numpy()
+    alg = algorithmic(cfg, tiers, ids, T)
+
+    for i in range(args.warmup):
+        fwd[i % R]()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(K):                     # create the events before the timed region
+        for e in ev[i]:
+            e.record(stream)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        L = layers[i % R]
+        L.set_stage_events(ev[i])
+        fwd[i % R]()
+    end.record(stream)
+    torch.cuda.synchronize()
+    for L in layers:
+        L.set_stage_events(None)
+    total_ms = start.elapsed_time(end)
+    stage_ms = np.array([[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(6)] for i in range(K)])
+    stage_avg_us = (stage_ms.mean(axis=0) * 1000).round(2)
+    ms_per_step = total_ms / K
+    value = T * K / (total_ms / 1000.0)
+    log("[bench] stage averages (us): " +
+        ", ".join(f"{n}={v}" for n, v in zip(STAGES, stage_avg_us)))
+
+    prefill = alg["flops13"] / (alg["bytes13"] / HBM_PEAK_GBS * 1e9) > BF16_PEAK_TFLOPS * 1e12
+    g13_s = stage_avg_us[3] * 1e-6
+    workload_key = f"cfg{cfg.cid}_T{T}"
+    if prefill:
+        achieved = alg["flops13"] / g13_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = alg["bytes13"] / g13_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "grouped_gemm gate/up + SwiGLU"
+    roof["avg_launch_us"] = float(stage_avg_us[3])
+    roof["algorithmic_per_launch"] = alg["flops13"] if prefill else alg["bytes13"]
+    roof["traffic"] = stored_traffic(workload_key)
+
+    layer_roof_s = max(alg["bytes_layer"] / (HBM_PEAK_GBS * 1e9),
+                       alg["flops_layer"] / (BF16_PEAK_TFLOPS * 1e12))
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.describe(T),
+            "tokens": T, "hidden": cfg.hidden, "experts": cfg.n_experts, "top_k": cfg.top_k,
+            "inter": cfg.inter, "touched_experts": alg["touched"],
+            "weight_copies_rotated": R, "output": args.out_dtype,
+            "layer_roofline_frac": round(layer_roof_s / (ms_per_step / 1000.0), 4),
+            "stage_avg_us": dict(zip(STAGES, [float(v) for v in stage_avg_us])),
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, tiers, x_np, wr_np, bias_np)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    for L in layers:
+        L.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -163,6 +163,27 @@ class Layer:
                                           _stream(stream)), "moe_layer_forward")
         return y
 
+    def bind_forward(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor],
+                     y: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None):
+        """A zero-argument callable that enqueues one forward with these fixed
+        buffers (arguments marshalled once; used for timing loops)."""
+        _require_cuda(x, "x", _BF16)
+        _require_cuda(wr, "wr", _BF16)
+        _require_cuda(y, "y", (torch.float32, torch.bfloat16))
+        ws = self.workspace(x.shape[0], x.device) if workspace is None else workspace
+        fn = self._lib.moe_layer_forward
+        args = (self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), x.shape[0], y.data_ptr(),
+                DTYPE_F32 if y.dtype == torch.float32 else DTYPE_BF16, ws.data_ptr(), ws.numel(),
+                _stream(stream))
+        keep = (x, wr, bias, y, ws)
+
+        def run():
+            rc = fn(*args)
+            if rc:
+                check(rc, "moe_layer_forward")
+            return keep
+        return run
+
     def set_stage_events(self, events: Optional[Sequence["torch.cuda.Event"]]) -> None:
         """Per-stage timing events (7 torch.cuda.Event with timing), or None."""
         if not events:

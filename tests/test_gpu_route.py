@@ -57,7 +57,7 @@ def test_route_k_equals_e():
 
 
 def test_route_large_bias_forces_experts():
-    st = Setup(2, T=48, bias=None)
+    st = Setup(2, T=32, bias=None)
     b = np.zeros(st.E, np.float32)
     b[[3, 77, 100, 101, 5, 9, 64, 127]] = 1000.0
     st.bias = b
