@@ -59,7 +59,7 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
   w.ntiles2 = take(sizeof(int32_t));
   w.r13 = take(sizeof(float) * T * (size_t)(L.H / kGroup));
   w.act = take(sizeof(uint16_t) * R * L.I);
-  w.r2 = take(sizeof(float) * R * (L.I / kGroup));
+  w.r2 = take(sizeof(float) * R * (L.I / 32));
   w.rows = take(sizeof(float) * R * L.H);
   w.total = o;
   return w;
@@ -318,10 +318,10 @@ hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, co
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos,
                          float* r13, void* ws, const Stages& st) {
   st.rec(0);
-  hipError_t e = launch_router_logits(x, wr, bias, T, L.H, L.E, logits, st.s);
+  hipError_t e = launch_router_logits(x, wr, bias, T, L.H, L.E, logits, r13, st.s);
   if (e != hipSuccess) return e;
   st.rec(1);
-  e = launch_topk(logits, x, T, L.H, L.E, L.k, ids, w, r13, st.s);
+  e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
   if (e != hipSuccess) return e;
   st.rec(2);
   return launch_permute(ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),

@@ -43,23 +43,80 @@ __device__ __forceinline__ u32x4 load_u32x4_stream(const void* p) {
   return u32x4{v[0], v[1], v[2], v[3]};
 }
 
+// Values the hardware holds once per wave (tile entries, expert handles): read
+// them from lane 0 so the compiler keeps them, and whatever is derived from
+// them, in scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer resource over [base, base + bytes): loads through it take their
+// offsets in an SGPR (wave-uniform part) plus one VGPR (per-lane part), and a
+// load outside the range returns zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16-byte load through a buffer resource; stream = non-temporal (read once).
+template <bool STREAM>
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, STREAM ? 2 : 0);
+  return u32x4{v[0], v[1], v[2], v[3]};
+}
+
+__device__ __forceinline__ uint16_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                    uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   v4u t = {v.x, v.y, v.z, v.w};
   return __builtin_bit_cast(bf16x8_t, t);
 }
 
+// The two constants of the int4 unpack, made opaque so the compiler keeps the
+// mask in an SGPR and the magic in a VGPR and can then select one VOP3
+// v_and_or_b32 per register (gfx9 VOP3 takes no literal operand).  Only the
+// constants come from asm; the and-or that feeds the MFMA is compiler-visible,
+// so the hazard recognizer still sees every VGPR write an MFMA reads.
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
+  return r;
+}
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+struct Int4Consts {
+  uint32_t mask, magic;
+};
+__device__ __forceinline__ Int4Consts int4_consts() {
+  return Int4Consts{opaque_sgpr(0x000f000fu), opaque_vgpr(0x43004300u)};
+}
+
 // Eight offset-binary int4 codes (nibble value q+8) of one MFMA k-chunk ->
 // eight bf16 operands of value 136 + q, exact.  Nibble j of the word holds
 // element 2j and nibble j+4 holds element 2j+1, so each output register is one
 // shift and one and-or: 0x4300 | u is the bf16 value 128 + u for u < 16.
-__device__ __forceinline__ bf16x8_t int4x8_to_bf16_biased(uint32_t w) {
+__device__ __forceinline__ bf16x8_t int4x8_to_bf16_biased(uint32_t w, Int4Consts c) {
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   v4u t;
-  t[0] = (w & 0x000f000fu) | 0x43004300u;
-  t[1] = ((w >> 4) & 0x000f000fu) | 0x43004300u;
-  t[2] = ((w >> 8) & 0x000f000fu) | 0x43004300u;
-  t[3] = ((w >> 12) & 0x000f000fu) | 0x43004300u;
+  t[0] = (w & c.mask) | c.magic;
+  t[1] = ((w >> 4) & c.mask) | c.magic;
+  t[2] = ((w >> 8) & c.mask) | c.magic;
+  t[3] = ((w >> 12) & c.mask) | c.magic;
   return __builtin_bit_cast(bf16x8_t, t);
 }
 

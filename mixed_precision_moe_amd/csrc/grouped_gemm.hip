@@ -28,6 +28,8 @@
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout used here: lane l holds row
 // (A) / column (B) l%16 and the 8 k-values 8*(l/16) .. +7 of the 32-wide step;
 // the accumulator of lane l holds rows 4*(l/16) + i, column l%16.
+#include <type_traits>
+
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -40,13 +42,13 @@ struct GemmArgs {
   const int32_t* ntiles;
   const uint16_t* a_src;     // gate/up: x [T, H]; down: act [T*k, I] in grouped order
   const int32_t* sorted;     // grouped route order (route ids t*k + j)
-  const float* rsum;         // gate/up: R13 [T, H/128] by token; down: R2 [T*k, I/128] by row
+  const float* rsum;         // gate/up: R13 [T, H/128] by token; down: R2 partials [T*k, I/32] by row
   int top_k;
   int K;                     // reduction size: H (gate/up) or I (down)
   int N;                     // output columns: 2I (gate/up) or H (down)
   // gate/up epilogue
   uint16_t* act;             // [T*k, I] bf16, grouped order
-  float* r2;                 // [T*k, I/128]
+  float* r2;                 // [T*k, I/32]: row sums of each 32-column block of act
   int I;
   // down epilogue
   const float* topk_w;       // [T*k] routing weights by route id
@@ -73,11 +75,26 @@ struct TierTraits<MOE_TIER_BF16> {
   static constexpr float kOffset = 0.0f;
 };
 
+// Activation sum of k-group g of one A row.  Gate/up: R13[token][g] (one value
+// per 128 inputs).  Down: the gate/up epilogue leaves one partial per 32
+// activation columns, so a 128-group is the sum of four, added in a fixed order.
+template <bool GATE_UP>
+__device__ __forceinline__ float row_sum(const float* r, int g) {
+  if (!r) return 0.0f;
+  if constexpr (GATE_UP) {
+    return r[g];
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(r + 4 * g);
+    return (v.x + v.y) + (v.z + v.w);
+  }
+}
+
 template <int TIER>
-__device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>::kLoads], int s) {
+__device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>::kLoads], int s,
+                                              Int4Consts c4) {
   if constexpr (TIER == MOE_TIER_INT4) {
     const uint32_t w = s == 0 ? b[0].x : s == 1 ? b[0].y : s == 2 ? b[0].z : b[0].w;
-    return int4x8_to_bf16_biased(w);
+    return int4x8_to_bf16_biased(w, c4);
   } else if constexpr (TIER == MOE_TIER_INT8) {
     const u32x4& h = b[s >> 1];
     return (s & 1) ? int8x8_to_bf16_biased(h.z, h.w) : int8x8_to_bf16_biased(h.x, h.y);
@@ -97,7 +114,7 @@ struct Tile {
   static constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
 };
 
-template <int TIER, int RT, int NS, int WN>
+template <int TIER, int RT, int NS, int WN, bool GATE_UP>
 __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, bool gate_up,
                                          int strip0, const uint16_t* const (&arow)[Tile<RT, NS, WN>::kChunksPerThread],
                                          const int (&acol)[Tile<RT, NS, WN>::kChunksPerThread],
@@ -106,6 +123,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
                                          f32x4_t (&acc)[RT][NS]) {
   using TT = Tile<RT, NS, WN>;
   using TR = TierTraits<TIER>;
+  const Int4Consts c4 = int4_consts();
   const int lane = threadIdx.x & 63;
   const int K = a.K, G = K / kGroup;
   const uint8_t* blob = gate_up ? h.w13 : h.w2;
@@ -169,7 +187,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
       for (int rt = 0; rt < RT; ++rt) {
         f32x4_t init;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) init[i] = rrow[rt][i] ? -TR::kOffset * rrow[rt][i][g] : 0.0f;
+        for (int i = 0; i < 4; ++i) init[i] = -TR::kOffset * row_sum<GATE_UP>(rrow[rt][i], g);
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) p[rt][ns] = init;
       }
@@ -184,7 +202,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
                                       8 * (lane >> 4)));
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) {
-        const bf16x8_t bf = b_operand<TIER>(b_cur[ns], s);
+        const bf16x8_t bf = b_operand<TIER>(b_cur[ns], s, c4);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) p[rt][ns] = mfma16x16x32(af[rt], bf, p[rt][ns]);
       }
@@ -225,7 +243,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
 template <int RT, int NS, int WN, bool GATE_UP>
 __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
   using TT = Tile<RT, NS, WN>;
-  static_assert(!GATE_UP || (NS % 4 == 0 && TT::BN == 256), "gate/up tile covers one 128-group of I");
+  static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
   const int tile_idx = blockIdx.y;
   if (tile_idx >= *a.ntiles) return;
   const TileEntry te = a.tiles[tile_idx];
@@ -235,7 +253,6 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
   const int strip0 = (n_block + wave * 16 * NS) / 16;
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TT::BM * kLdsStride];
-  __shared__ float part[WN][TT::BM];
 
   // A staging role of this thread: chunk c -> (row, 16-byte column)
   const uint16_t* arow[TT::kChunksPerThread];
@@ -272,7 +289,7 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
         if constexpr (GATE_UP)
           rrow[rt][i] = a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G;
         else
-          rrow[rt][i] = a.rsum + (size_t)pos * G;
+          rrow[rt][i] = a.rsum + (size_t)pos * (a.K / 32);
       }
     }
 
@@ -284,13 +301,13 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
 
   switch (h.tier) {
     case MOE_TIER_INT4:
-      mainloop<MOE_TIER_INT4, RT, NS, WN>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
+      mainloop<MOE_TIER_INT4, RT, NS, WN, GATE_UP>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
       break;
     case MOE_TIER_INT8:
-      mainloop<MOE_TIER_INT8, RT, NS, WN>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
+      mainloop<MOE_TIER_INT8, RT, NS, WN, GATE_UP>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
       break;
     default:
-      mainloop<MOE_TIER_BF16, RT, NS, WN>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
+      mainloop<MOE_TIER_BF16, RT, NS, WN, GATE_UP>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
       break;
   }
 
@@ -321,8 +338,9 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
           }
       }
     }
-    // per-row sums of this block's 128 activation columns (one k-group of the
-    // down GEMM), reduced in a fixed order: lanes, then waves.
+    // per-row sums of this wave's 32 activation columns (fixed order: strips,
+    // then a butterfly over the 16 lanes of a row group)
+    const int P = a.I / 32;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -330,16 +348,10 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
         float v = rs[rt][i];
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
-        if ((lane & 15) == 0) part[wave][16 * rt + 4 * (lane >> 4) + i] = v;
+        const int m = 16 * rt + 4 * (lane >> 4) + i;
+        if ((lane & 15) == 0 && m < te.rows)
+          a.r2[(size_t)(te.row_start + m) * P + strip0 / 4] = v;
       }
-    __syncthreads();
-    const int G2 = a.I / kGroup;
-    for (int m = threadIdx.x; m < te.rows && m < TT::BM; m += TT::kThreads) {
-      float v = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WN; ++w) v += part[w][m];
-      a.r2[(size_t)(te.row_start + m) * G2 + blockIdx.x] = v;
-    }
   } else {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -355,6 +367,239 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
         }
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel: few rows per expert (an M-tile of at most 16 routes), so the
+// cost is streaming the expert's weights from HBM.  A block of WAVES waves
+// owns one M-tile and WAVES * NS consecutive 16-column strips.  Its A rows
+// (only the tile's real rows, all of K) and their group sums are staged into
+// LDS once, while every wave already has its first weight loads in flight;
+// after that single barrier each wave streams its strips over the whole K with
+// the next D k-groups of weights and scales in flight, reading A fragments
+// from LDS (rows beyond the tile's count are zero and never read).  For a
+// gate/up matrix NS = 4 covers 32 gate and the matching 32 up columns.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeRows = 8;   // rows of an M-tile in the decode kernel (MFMA rows 8..15 are zero)
+constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
+
+template <int TIER, int NS, int WAVES, bool GATE_UP>
+__device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEntry& te,
+                                                const uint8_t* blob, int strip0, uint16_t* lds_a,
+                                                float* lds_r, f32x4_t (&acc)[NS]) {
+  using TR = TierTraits<TIER>;
+  const Int4Consts c4 = int4_consts();
+  constexpr int D = TIER == MOE_TIER_INT4 ? 2 : 1;
+  constexpr int L = TR::kLoads;
+  const int lane = threadIdx.x & 63;
+  const int K = a.K, G = K / kGroup;
+  const int lda = K + 8;                      // LDS row stride (bf16)
+  const int rows = te.rows;
+  const uint32_t code_bytes = (uint32_t)((size_t)a.N * K * TR::kTileBytes / (16 * kGroup));
+  const uint32_t blob_bytes = code_bytes + (TIER == MOE_TIER_INT4 ? (uint32_t)a.N * G * 2
+                                            : TIER == MOE_TIER_INT8 ? (uint32_t)a.N * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_bytes);
+
+  u32x4 bb[D][NS][L];
+  uint16_t sc[D][NS];
+  auto issue = [&](int g, int d) {
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const uint32_t tile = (uint32_t)((strip0 + ns) * G + g);
+#pragma unroll
+      for (int q = 0; q < L; ++q)
+        bb[d][ns][q] = buffer_load16<true>(rsrc, 16 * lane + 1024 * q, tile * TR::kTileBytes);
+      if constexpr (TIER == MOE_TIER_INT4)
+        sc[d][ns] = buffer_load_u16(rsrc, 2 * (lane & 15), code_bytes + tile * 32);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < G) issue(d, d);
+
+  // stage A rows and group sums of this tile (block-wide, once)
+  {
+    const int chunks = rows * (K / 8);
+    for (int c = threadIdx.x; c < chunks; c += 64 * WAVES) {
+      const int m = c / (K / 8), col = 8 * (c - m * (K / 8));
+      const int pos = te.row_start + m;
+      const uint16_t* src = GATE_UP ? a.a_src + (size_t)(a.sorted[pos] / a.top_k) * K + col
+                                    : a.a_src + (size_t)pos * K + col;
+      *reinterpret_cast<uint4*>(lds_a + m * lda + col) = *reinterpret_cast<const uint4*>(src);
+    }
+    if constexpr (TIER != MOE_TIER_BF16) {
+      for (int i = threadIdx.x; i < G * kRStride; i += 64 * WAVES) {
+        const int g = i / kRStride, m = i - g * kRStride;
+        float r = 0.0f;
+        if (m < rows) {
+          const int pos = te.row_start + m;
+          r = GATE_UP ? row_sum<true>(a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G, g)
+                      : row_sum<false>(a.rsum + (size_t)pos * (K / 32), g);
+        }
+        lds_r[i] = r;
+      }
+    }
+  }
+  __syncthreads();
+
+  float row_scale[NS];
+  if constexpr (TIER == MOE_TIER_INT8) {
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+      row_scale[ns] = (float)__builtin_bit_cast(
+          _Float16, buffer_load_u16(rsrc, 2 * (lane & 15), code_bytes + 32 * (strip0 + ns)));
+  }
+  const bool arow_ok = (lane & 15) < rows;
+  const uint16_t* la = lds_a + (lane & 15) * lda + 8 * (lane >> 4);
+
+#pragma nounroll
+  for (int g0 = 0; g0 < G; g0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int g = g0 + d;
+      if (g >= G) break;
+      f32x4_t p[NS];
+      if constexpr (TIER == MOE_TIER_BF16) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) p[ns] = acc[ns];
+      } else {
+        const float4 r4 = *reinterpret_cast<const float4*>(lds_r + g * kRStride + 4 * (lane >> 4));
+        const f32x4_t init = {-TR::kOffset * r4.x, -TR::kOffset * r4.y, -TR::kOffset * r4.z,
+                              -TR::kOffset * r4.w};
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) p[ns] = init;
+      }
+      bf16x8_t af[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        af[s4] = as_bf16x8(arow_ok ? load_u32x4(la + kGroup * g + 32 * s4) : u32x4{0, 0, 0, 0});
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) p[ns] = mfma16x16x32(af[s4], b_operand<TIER>(bb[d][ns], s4, c4), p[ns]);
+      if constexpr (TIER == MOE_TIER_BF16) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) acc[ns] = p[ns];
+      } else {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+          float scf;
+          if constexpr (TIER == MOE_TIER_INT4)
+            scf = (float)__builtin_bit_cast(_Float16, sc[d][ns]);
+          else
+            scf = row_scale[ns];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(scf, p[ns][i], acc[ns][i]);
+        }
+      }
+      if (g + D < G) issue(g + D, d);
+    }
+  }
+}
+
+template <int NS, int WAVES, bool GATE_UP>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
+  static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+  const int tile_idx = blockIdx.x / blocks_per_tile;
+  const int nb = blockIdx.x - tile_idx * blocks_per_tile;
+  if (tile_idx >= uniform(*a.ntiles)) return;
+  TileEntry te = a.tiles[tile_idx];
+  te.expert = uniform(te.expert);
+  te.row_start = uniform(te.row_start);
+  te.rows = uniform(te.rows);
+  DevHandle h = a.table[te.expert];
+  h.tier = uniform(h.tier);
+  h.w13 = uniform_ptr(h.w13);
+  h.w2 = uniform_ptr(h.w2);
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int chunk = nb * WAVES + wave;       // this wave's group of NS strips
+  const int strip0 = chunk * NS;
+  uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
+  float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)kDecodeRows * (a.K + 8) * 2);
+
+  f32x4_t acc[NS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* blob = GATE_UP ? h.w13 : h.w2;
+  switch (h.tier) {
+    case MOE_TIER_INT4:
+      decode_mainloop<MOE_TIER_INT4, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
+      break;
+    case MOE_TIER_INT8:
+      decode_mainloop<MOE_TIER_INT8, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
+      break;
+    default:
+      decode_mainloop<MOE_TIER_BF16, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
+      break;
+  }
+
+  if constexpr (GATE_UP) {
+    // SwiGLU on strips (0,2) and (1,3): gate and up of 32 activation columns
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int icol = 32 * chunk + 16 * half + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * (lane >> 4) + i;
+        const uint32_t a16 = f32_to_bf16_rne(silu_f32(acc[half][i]) * acc[half + 2][i]);
+        if (m < te.rows) {
+          a.act[(size_t)(te.row_start + m) * a.I + icol] = (uint16_t)a16;
+          rs[i] += bf16_to_f32(a16);
+        }
+      }
+    }
+    const int P = a.I / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = rs[i];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+      const int m = 4 * (lane >> 4) + i;
+      if ((lane & 15) == 0 && m < te.rows) a.r2[(size_t)(te.row_start + m) * P + chunk] = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * (lane >> 4) + i;
+      if (m < te.rows) {
+        const int pos = te.row_start + m;
+        const float wgt = a.topk_w[a.sorted[pos]];
+        float* out = a.rows + (size_t)pos * a.N + 16 * strip0 + (lane & 15);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) out[16 * ns] = wgt * acc[ns][i];
+      }
+    }
+  }
+}
+
+size_t decode_lds_bytes(int K) {
+  return (size_t)kDecodeRows * (K + 8) * 2 + (size_t)(K / kGroup) * kRStride * 4;
+}
+
+template <int NS, bool GATE_UP>
+hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s) {
+  // waves per block: as many strips of one tile as divide N evenly, up to 8
+  const int strips = a.N / 16;
+  const int chunks = strips / NS;
+  const size_t lds = decode_lds_bytes(a.K);
+  static bool attr_set[2] = {false, false};
+  auto run = [&](auto waves_c) -> hipError_t {
+    constexpr int W = decltype(waves_c)::value;
+    auto kern = gemm_decode_kernel<NS, W, GATE_UP>;
+    if (!attr_set[W == 8]) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+      if (e != hipSuccess) return e;
+      attr_set[W == 8] = true;
+    }
+    const int bpt = chunks / W;
+    hipLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), lds, s, a, bpt);
+    return hipGetLastError();
+  };
+  return run(std::integral_constant<int, 4>{});   // N is a multiple of 256: chunks % 4 == 0
 }
 
 template <int RT, bool GATE_UP>
@@ -396,10 +641,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
   const double rows_per_expert = (double)T * L.k / L.E;
-  const int bm = rows_per_expert <= 16.0 ? 16 : 64;
-  p.bm13 = bm;
-  p.bm2 = bm;
-  p.kind = 0;
+  const bool decode = rows_per_expert <= 4.0;
+  p.kind = decode ? 1 : 0;
+  p.bm13 = decode ? kDecodeRows : 64;
+  p.bm2 = p.bm13;
   return p;
 }
 
@@ -421,7 +666,7 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.act = act;
   a.r2 = r2;
   a.I = L.I;
-  if (gp.bm13 == 16) return launch_gg<1, true>(a, max_tiles, s);
+  if (gp.kind == 1) return launch_decode<4, true>(a, max_tiles, s);
   return launch_gg<4, true>(a, max_tiles, s);
 }
 
@@ -442,7 +687,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.N = L.H;
   a.topk_w = topk_w;
   a.rows = rows;
-  if (gp.bm2 == 16) return launch_gg<1, false>(a, max_tiles, s);
+  if (gp.kind == 1) return launch_decode<4, false>(a, max_tiles, s);
   return launch_gg<4, false>(a, max_tiles, s);
 }
 

@@ -68,9 +68,9 @@ hipError_t launch_quantize_pack(int tier, int layout, const uint16_t* w, int64_t
 hipError_t launch_set_handles(DevHandle* table, int first, int count,
                               const moe_expert_handle* h, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
-                                int T, int H, int E, float* logits, hipStream_t s);
-hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int k,
-                       int32_t* ids, float* w, float* r13, hipStream_t s);
+                                int T, int H, int E, float* logits, float* r13, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
                           int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,

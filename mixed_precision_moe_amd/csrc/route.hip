@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
                                                             int T, int H, int E,
-                                                            float* __restrict__ logits) {
+                                                            float* __restrict__ logits,
+                                                            float* __restrict__ r13) {
   const int j = threadIdx.x & 31;           // chain index
   const int hw = threadIdx.x >> 5;          // half-wave 0..7
   const int t0 = blockIdx.x * (2 * TT) + (hw >> 2) * TT;
@@ -43,6 +44,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
     for (int b = 0; b < TE; ++b) acc[a][b] = 0.0f;
 
+  // Half-waves of expert group 0 also produce R13[t][g] = sum of the 128
+  // activations of group g (used by the GEMMs to remove their weight offset).
+  const bool do_r13 = r13 != nullptr && blockIdx.y == 0 && (hw & 3) == 0;
+  const int G = H / kGroup;
   for (int base = 0; base < H; base += 256) {
     u32x4 xv[TT], wv[TE];
 #pragma unroll
@@ -66,6 +71,18 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       for (int a = 0; a < TT; ++a)
 #pragma unroll
         for (int b = 0; b < TE; ++b) acc[a][b] = __builtin_fmaf(xf[a], wf[b], acc[a][b]);
+    }
+    if (do_r13) {
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        const u32x4 q = xv[a];
+        float v = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
+                  (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+        const int t = t0 + a;
+        if ((j & 15) == 0 && t < T) r13[(size_t)t * G + base / kGroup + (j >> 4)] = v;
+      }
     }
   }
   // fold the 32 chains: chain j += chain j+s, s = 16 .. 1
@@ -98,19 +115,21 @@ __device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
   return va > vb || (va == vb && ea < eb);
 }
 
+extern "C" __device__ float __ockl_wfred_max_f32(float);
+extern "C" __device__ int __ockl_wfred_min_i32(int);
+
 // One wave per token: select the k largest logits (ties -> lower id), softmax
-// over them, store ids ascending with their weights.  Also the per-group sums
-// of the token's activations, R13[t][g] = sum_{h in group g} x[t][h] (used by
-// the GEMM to remove the offset of its biased weight operands).
+// over them, store ids ascending with their weights.  Each round takes the
+// lane-local best of the not-yet-taken experts (lane l holds experts
+// l, l+64, ...), a wave max of the logit (DPP reduction), and, only if several
+// lanes hold that maximum, a wave min of their expert ids.
 constexpr int kMaxPerLane = kMaxExperts / 64;
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
-                                                   const uint16_t* __restrict__ x, int T, int H,
-                                                   int E, int k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ weights,
-                                                   float* __restrict__ r13) {
+__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                  int k, int32_t* __restrict__ ids,
+                                                  float* __restrict__ weights) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x;
   if (t >= T) return;
   const float* z = logits + (size_t)t * E;
   float v[kMaxPerLane];
@@ -136,32 +155,31 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         be = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (be >= E) be = jj;   // only reachable with NaN logits (out of domain): stay in bounds
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    sel_e[jj] = be;
-    sel_z[jj] = bv;
+    const float wmax = __ockl_wfred_max_f32(bv);
+    const bool cand = bv == wmax && be < E;
+    const uint64_t mask = __ballot(cand);
+    int we;
+    if (__popcll(mask) == 1)
+      we = __builtin_amdgcn_readlane(be, __ffsll((unsigned long long)mask) - 1);
+    else
+      we = __ockl_wfred_min_i32(cand ? be : 0x7fffffff);
+    if (we >= E || we < 0) we = jj;   // only reachable with NaN logits (out of domain)
+    if ((we & 63) == lane) taken |= 1u << (we >> 6);
+    sel_e[jj] = we;
+    sel_z[jj] = wmax;
   }
   // softmax over the selected logits (the first selected one is the largest)
   if (lane < k) {
     int my_e = 0;
-    double my_z = 0.0, den = 0.0;
-    const double zmax = (double)sel_z[0];
+    float my_z = 0.0f, den = 0.0f;
+    const float zmax = sel_z[0];
 #pragma unroll
     for (int jj = 0; jj < kMaxTopK; ++jj) {
       if (jj >= k) break;
-      den += exp((double)sel_z[jj] - zmax);
+      den += expf(sel_z[jj] - zmax);
       if (jj == lane) {
         my_e = sel_e[jj];
-        my_z = (double)sel_z[jj];
+        my_z = sel_z[jj];
       }
     }
     int rank = 0;
@@ -171,25 +189,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       rank += sel_e[jj] < my_e;
     }
     ids[(size_t)t * k + rank] = my_e;
-    weights[(size_t)t * k + rank] = (float)(exp(my_z - zmax) / den);
+    weights[(size_t)t * k + rank] = expf(my_z - zmax) / den;
   }
-  if (r13) {
-    // group g, 16 lanes x 8 elements; four groups per pass
-    const uint16_t* xr = x + (size_t)t * H;
-    const int G = H / kGroup;
-    for (int g0 = 0; g0 < G; g0 += 4) {
-      const int g = g0 + (lane >> 4);
-      float s = 0.0f;
-      if (g < G) {
-        const u32x4 q = load_u32x4(xr + kGroup * g + 8 * (lane & 15));
-        s = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
-            (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
-      }
+}
+
+// Exclusive prefix sum over the 1024 threads of a block; also returns the total.
+// Wave-level inclusive scan with shuffles, then one pass over the 16 wave totals.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
-      if (g < G && (lane & 15) == 0) r13[(size_t)t * G + g] = s;
-    }
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
   }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int t = wave_tot[w];
+    base += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();   // wave_tot may be reused by the caller's next scan
+  total = tot;
+  return base + inc - v;
 }
 
 // Grouping by expert in one workgroup of 1024 threads (16 waves).
@@ -231,19 +256,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   __syncthreads();
 
   // exclusive scan of totals over experts (E <= 1024: one value per thread)
-  const int mytot = tid < E ? off[tid] : 0;
-  scan[tid] = mytot;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int add = tid >= d ? scan[tid - d] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int excl = scan[tid] - mytot;   // exclusive prefix
-  __syncthreads();
+  int total = 0;
+  const int excl = block_exclusive_scan(tid < E ? off[tid] : 0, scan, total);
   if (tid < E) off[tid] = excl;
-  if (tid == 0) off[E] = scan[1023];
+  if (tid == 0) off[E] = total;
   __syncthreads();
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
 
@@ -268,15 +284,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     int32_t* ntiles = table == 0 ? ntiles13 : ntiles2;
     const int ce = tid < E ? off[tid + 1] - off[tid] : 0;
     const int nt = (ce + bm - 1) / bm;
-    scan[tid] = nt;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const int add = tid >= d ? scan[tid - d] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    const int first = scan[tid] - nt;
+    int tot = 0;
+    const int first = block_exclusive_scan(nt, scan, tot);
     for (int i = 0; i < nt; ++i) {
       TileEntry te2;
       te2.expert = tid;
@@ -285,33 +294,31 @@ __global__ __launch_bounds__(1024) void permute_kernel(
       te2.pad = 0;
       tiles[first + i] = te2;
     }
-    if (tid == 1023) *ntiles = scan[1023];
-    __syncthreads();
+    if (tid == 0) *ntiles = tot;
   }
 }
 
 }  // namespace
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
-                                int H, int E, float* logits, hipStream_t s) {
+                                int H, int E, float* logits, float* r13, hipStream_t s) {
   if (T <= 64) {
     constexpr int TT = 1, TE = 4;
     const dim3 grid((T + 2 * TT - 1) / (2 * TT), (E + 4 * TE - 1) / (4 * TE));
     hipLaunchKernelGGL((router_logits_kernel<TT, TE>), grid, dim3(256), 0, s, x, wr, bias, T, H,
-                       E, logits);
+                       E, logits, r13);
   } else {
     constexpr int TT = 4, TE = 4;
     const dim3 grid((T + 2 * TT - 1) / (2 * TT), (E + 4 * TE - 1) / (4 * TE));
     hipLaunchKernelGGL((router_logits_kernel<TT, TE>), grid, dim3(256), 0, s, x, wr, bias, T, H,
-                       E, logits);
+                       E, logits, r13);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, const uint16_t* x, int T, int H, int E, int k,
-                       int32_t* ids, float* w, float* r13, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, H, E, k, ids,
-                     w, r13);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
