@@ -110,14 +110,15 @@ typedef struct moe_layer_s* moe_layer_t;
  * rounded up to a multiple of 256.  int4: n*k/2 + 2*n*k/128 (exactly the
  * ExactMoE §3.2 memory equation); int8: n*k + 2*n; bf16: 2*n*k.
  * Returns 0 for a bad tier or a shape the layout cannot hold
- * (k_in % 128 != 0 or n_out % 16 != 0). */
+ * (k_in % 128 != 0 or n_out % 64 != 0). */
 size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in);
 
 /* Quantize (ExactMoE §3.2; int8: the same rule per row with range +-127) and
  * pack one matrix into the kernel's layout, on the GPU.
  *   w_bf16    device, [n_out, k_in] bf16 master weight (PyTorch Linear layout).
- *   layout    MOE_LAYOUT_PLAIN or MOE_LAYOUT_GATE_UP (then n_out = 2I with
- *             I % 32 == 0 and rows 0..I-1 the gate, I..2I-1 the up projection).
+ *   layout    MOE_LAYOUT_PLAIN or MOE_LAYOUT_GATE_UP (then n_out = 2I and
+ *             rows 0..I-1 are the gate, I..2I-1 the up projection).
+ *   n_out % 64 == 0, k_in % 128 == 0, 2 * n_out * k_in < 4 GiB (MOE_ESHAPE).
  *   dst       device, 256-byte aligned, dst_bytes >= moe_packed_size(...).
  * Scales are fp16 (nearest-even of the fp32 quotient max/7 or max/127); codes
  * use round-half-to-even of w / scale.  This is set-up work, not the hot path:

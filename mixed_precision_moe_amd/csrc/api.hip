@@ -136,7 +136,7 @@ const char* moe_strerror(int status) {
 const char* moe_last_error(void) { return g_err; }
 
 size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in) {
-  if (n_out <= 0 || k_in <= 0 || k_in % kGroup || n_out % 16) return 0;
+  if (n_out <= 0 || k_in <= 0 || k_in % kGroup || n_out % 64) return 0;
   size_t bytes;
   switch (tier) {
     case MOE_TIER_INT4: bytes = (size_t)n_out * k_in / 2 + (size_t)n_out * (k_in / kGroup) * 2; break;
@@ -157,12 +157,12 @@ int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_ou
   if (!w_bf16 || !dst) return set_error(MOE_EINVAL, "null pointer");
   if (!aligned(dst, kBlobAlign)) return set_error(MOE_EINVAL, "dst must be 256-byte aligned");
   if (!aligned(w_bf16, 16)) return set_error(MOE_EINVAL, "weights must be 16-byte aligned");
-  if (n_out <= 0 || k_in <= 0 || k_in % kGroup || n_out % 16 || n_out > (1 << 30) ||
+  if (n_out <= 0 || k_in <= 0 || k_in % kGroup || n_out % 64 || n_out > (1 << 30) ||
       k_in > (1 << 30))
-    return set_error(MOE_ESHAPE, "need k_in %% 128 == 0 and n_out %% 16 == 0 (got %lld x %lld)",
+    return set_error(MOE_ESHAPE, "need k_in %% 128 == 0 and n_out %% 64 == 0 (got %lld x %lld)",
                      (long long)n_out, (long long)k_in);
-  if (layout == MOE_LAYOUT_GATE_UP && n_out % 64)
-    return set_error(MOE_ESHAPE, "gate/up layout needs n_out = 2I with I %% 32 == 0");
+  if ((uint64_t)n_out * (uint64_t)k_in * 2 > 0xffffffffull)
+    return set_error(MOE_ESHAPE, "a packed matrix must stay below 4 GiB");
   const size_t need = moe_packed_size(tier, n_out, k_in);
   if (dst_bytes < need)
     return set_error(MOE_ENOSPC, "dst has %zu bytes, %zu needed", dst_bytes, need);

@@ -72,6 +72,18 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return u32x4{v[0], v[1], v[2], v[3]};
 }
 
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// fp16 value j (0..3) of four packed in a uint2, as fp32
+__device__ __forceinline__ float half_of(uint2 v, int j) {
+  const uint32_t w = j < 2 ? v.x : v.y;
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+
 __device__ __forceinline__ uint16_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                                     uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);

@@ -59,21 +59,31 @@ constexpr int kLdsStride = kGroup + 8;   // bf16 per LDS row (272 B: conflict-fr
 
 template <int TIER>
 struct TierTraits;
+// Per tier: 16-byte loads per lane per strip and k-group, bytes of one strip's
+// tile, bytes of one (quad, k-group) block, weight offset of the codes.
 template <>
 struct TierTraits<MOE_TIER_INT4> {
-  static constexpr int kLoads = 1, kTileBytes = 1024;
+  static constexpr int kLoads = 1, kTileBytes = 1024, kBlockBytes = 4224;
   static constexpr float kOffset = 136.0f;
 };
 template <>
 struct TierTraits<MOE_TIER_INT8> {
-  static constexpr int kLoads = 2, kTileBytes = 2048;
+  static constexpr int kLoads = 2, kTileBytes = 2048, kBlockBytes = 8192;
   static constexpr float kOffset = 128.0f;
 };
 template <>
 struct TierTraits<MOE_TIER_BF16> {
-  static constexpr int kLoads = 4, kTileBytes = 4096;
+  static constexpr int kLoads = 4, kTileBytes = 4096, kBlockBytes = 16384;
   static constexpr float kOffset = 0.0f;
 };
+
+// Bytes of a packed [N, K] blob of one tier (without the 256-byte padding).
+template <int TIER>
+__device__ __forceinline__ uint32_t blob_payload(int N, int K) {
+  if constexpr (TIER == MOE_TIER_INT4) return (uint32_t)(N / 64) * (K / kGroup) * 4224u;
+  else if constexpr (TIER == MOE_TIER_INT8) return (uint32_t)N * K + 2u * N;
+  else return 2u * N * K;
+}
 
 // Activation sum of k-group g of one A row.  Gate/up: R13[token][g] (one value
 // per 128 inputs).  Down: the gate/up epilogue leaves one partial per 32
@@ -127,30 +137,28 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
   const int lane = threadIdx.x & 63;
   const int K = a.K, G = K / kGroup;
   const uint8_t* blob = gate_up ? h.w13 : h.w2;
-  const uint8_t* codes = blob;   // codes first, then the fp16 scales
-  const uint16_t* scales16 = nullptr;
-  if constexpr (TIER == MOE_TIER_INT4)
-    scales16 = reinterpret_cast<const uint16_t*>(blob + (size_t)a.N * K / 2);
-  else if constexpr (TIER == MOE_TIER_INT8)
-    scales16 = reinterpret_cast<const uint16_t*>(blob + (size_t)a.N * K);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_payload<TIER>(a.N, K));
+  const int quad = strip0 >> 2;          // NS = 4 strips = one quad of the layout
 
   float row_scale[NS];
   if constexpr (TIER == MOE_TIER_INT8) {
+    const uint2 rs4 = buffer_load8(rsrc, 8 * (lane & 15), (uint32_t)a.N * K + 128u * quad);
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-      row_scale[ns] = (float)__builtin_bit_cast(_Float16, scales16[16 * (strip0 + ns) + (lane & 15)]);
+    for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, ns);
   }
 
   u32x4 b_cur[NS][TR::kLoads], b_nxt[NS][TR::kLoads];
   u32x4 a_nxt[TT::kChunksPerThread];
 
-  auto load_b = [&](int g, u32x4 (&dst)[NS][TR::kLoads]) {
+  uint2 s_cur = make_uint2(0, 0), s_nxt = make_uint2(0, 0);   // int4 group scales
+  auto load_b = [&](int g, u32x4 (&dst)[NS][TR::kLoads], uint2& sdst) {
+    const uint32_t block = (uint32_t)(quad * G + g) * TR::kBlockBytes;
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const uint8_t* tp = codes + ((size_t)(strip0 + ns) * G + g) * TR::kTileBytes + 16 * lane;
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-      for (int q = 0; q < TR::kLoads; ++q) dst[ns][q] = load_u32x4_stream(tp + 1024 * q);
-    }
+      for (int q = 0; q < TR::kLoads; ++q)
+        dst[ns][q] = buffer_load16<true>(rsrc, 16 * lane + 1024 * q + ns * TR::kTileBytes, block);
+    if constexpr (TIER == MOE_TIER_INT4) sdst = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
   };
   auto load_a = [&](int g) {
 #pragma unroll
@@ -165,7 +173,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
             make_uint4(a_nxt[c].x, a_nxt[c].y, a_nxt[c].z, a_nxt[c].w);
   };
 
-  load_b(0, b_cur);
+  load_b(0, b_cur, s_cur);
   load_a(0);
   store_a(0);
   __syncthreads();
@@ -173,7 +181,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
   for (int g = 0; g < G; ++g) {
     const int buf = g & 1;
     if (g + 1 < G) {
-      load_b(g + 1, b_nxt);
+      load_b(g + 1, b_nxt, s_nxt);
       load_a(g + 1);
     }
     f32x4_t p[RT][NS];
@@ -214,13 +222,12 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
         for (int ns = 0; ns < NS; ++ns) acc[rt][ns] = p[rt][ns];
     } else {
       float sc[NS];
+      if constexpr (TIER == MOE_TIER_INT4) {
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        if constexpr (TIER == MOE_TIER_INT4)
-          sc[ns] = (float)__builtin_bit_cast(
-              _Float16, scales16[((size_t)(strip0 + ns) * G + g) * 16 + (lane & 15)]);
-        else
-          sc[ns] = row_scale[ns];
+        for (int ns = 0; ns < NS; ++ns) sc[ns] = half_of(s_cur, ns);
+      } else {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) sc[ns] = row_scale[ns];
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -235,6 +242,7 @@ __device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, 
       for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
         for (int q = 0; q < TR::kLoads; ++q) b_cur[ns][q] = b_nxt[ns][q];
+      s_cur = s_nxt;
     }
     __syncthreads();
   }
@@ -245,10 +253,16 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
   using TT = Tile<RT, NS, WN>;
   static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
   const int tile_idx = blockIdx.y;
-  if (tile_idx >= *a.ntiles) return;
-  const TileEntry te = a.tiles[tile_idx];
-  const DevHandle h = a.table[te.expert];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (tile_idx >= uniform(*a.ntiles)) return;
+  TileEntry te = a.tiles[tile_idx];
+  te.expert = uniform(te.expert);
+  te.row_start = uniform(te.row_start);
+  te.rows = uniform(te.rows);
+  DevHandle h = a.table[te.expert];
+  h.tier = uniform(h.tier);
+  h.w13 = uniform_ptr(h.w13);
+  h.w2 = uniform_ptr(h.w2);
+  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n_block = blockIdx.x * TT::BN;
   const int strip0 = (n_block + wave * 16 * NS) / 16;
 
@@ -395,23 +409,19 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   const int K = a.K, G = K / kGroup;
   const int lda = K + 8;                      // LDS row stride (bf16)
   const int rows = te.rows;
-  const uint32_t code_bytes = (uint32_t)((size_t)a.N * K * TR::kTileBytes / (16 * kGroup));
-  const uint32_t blob_bytes = code_bytes + (TIER == MOE_TIER_INT4 ? (uint32_t)a.N * G * 2
-                                            : TIER == MOE_TIER_INT8 ? (uint32_t)a.N * 2 : 0u);
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_payload<TIER>(a.N, K));
+  const int quad = strip0 >> 2;          // NS = 4 strips = one quad of the layout
 
   u32x4 bb[D][NS][L];
-  uint16_t sc[D][NS];
+  uint2 sc[D];
   auto issue = [&](int g, int d) {
+    const uint32_t block = (uint32_t)(quad * G + g) * TR::kBlockBytes;
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const uint32_t tile = (uint32_t)((strip0 + ns) * G + g);
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int q = 0; q < L; ++q)
-        bb[d][ns][q] = buffer_load16<true>(rsrc, 16 * lane + 1024 * q, tile * TR::kTileBytes);
-      if constexpr (TIER == MOE_TIER_INT4)
-        sc[d][ns] = buffer_load_u16(rsrc, 2 * (lane & 15), code_bytes + tile * 32);
-    }
+        bb[d][ns][q] = buffer_load16<true>(rsrc, 16 * lane + 1024 * q + ns * TR::kTileBytes, block);
+    if constexpr (TIER == MOE_TIER_INT4) sc[d] = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
   };
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -444,10 +454,9 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 
   float row_scale[NS];
   if constexpr (TIER == MOE_TIER_INT8) {
+    const uint2 rs4 = buffer_load8(rsrc, 8 * (lane & 15), (uint32_t)a.N * K + 128u * quad);
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-      row_scale[ns] = (float)__builtin_bit_cast(
-          _Float16, buffer_load_u16(rsrc, 2 * (lane & 15), code_bytes + 32 * (strip0 + ns)));
+    for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, ns);
   }
   const bool arow_ok = (lane & 15) < rows;
   const uint16_t* la = lds_a + (lane & 15) * lda + 8 * (lane >> 4);
@@ -485,7 +494,7 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
         for (int ns = 0; ns < NS; ++ns) {
           float scf;
           if constexpr (TIER == MOE_TIER_INT4)
-            scf = (float)__builtin_bit_cast(_Float16, sc[d][ns]);
+            scf = half_of(sc[d], ns);
           else
             scf = row_scale[ns];
 #pragma unroll

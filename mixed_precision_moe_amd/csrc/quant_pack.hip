@@ -7,17 +7,19 @@
 // quotient max/7 (or /127) rounded to fp16, and codes are taken against that
 // stored scale.
 //
-// Packed layout v1 (the kernels' operand order on gfx950): 16-row strips x
-// 128-column groups; inside a tile lane l = 16c + r owns row r and, for each of
-// the four 32-wide MFMA k-steps s, the 8 columns 32s + 8c .. +7.
-//   int4: tile 1024 B, lane bytes 16l..16l+15, step s = 32-bit word s, element i
-//         in nibble (i/2) + 4(i%2), nibble value q+8; fp16 scales after all
-//         codes at index (strip*G + g)*16 + r.
-//   int8: tile 2048 B, step s in half s/2 at 1024*(s/2) + 16l + 8(s%2) + i,
-//         byte value q+128; fp16 row scales after all codes.
-//   bf16: tile 4096 B, step s at 1024*s + 16l + 2i.
+// Packed layout v2 (the kernels' operand order on gfx950): 16-row strips t,
+// grouped in quads Q = t/4 (u = t%4), x 128-column groups g.  Inside a tile
+// lane l = 16c + r owns row r and, for each of the four 32-wide MFMA k-steps s,
+// the 8 columns 32s + 8c .. +7.  Per (Q, g) one contiguous block:
+//   int4: 4224 B = tiles u at 1024u (lane bytes 16l..16l+15, step s = 32-bit
+//         word s, element i in nibble (i/2) + 4(i%2), nibble value q+8), then
+//         the 64 fp16 group scales at 4096 + 2(4r + u);
+//   int8: 8192 B = tiles u at 2048u, step s in half s/2 at 1024(s/2) + 16l +
+//         8(s%2) + i, byte value q+128; fp16 row scales after all codes at
+//         element 64Q + 4r + u;
+//   bf16: 16384 B = tiles u at 4096u, step s at 1024s + 16l + 2i.
 // Gate/up matrices ([2I, H], gate rows first) are stored with gate and up rows
-// interleaved in blocks of 32 so one 64-row block holds gate and up of the same
+// interleaved in blocks of 32 so one 64-row quad holds gate and up of the same
 // 32 intermediate channels.
 #include "device_util.h"
 #include "moe_internal.h"
@@ -75,8 +77,7 @@ __global__ __launch_bounds__(256) void quant_pack_int4(const uint16_t* __restric
   const int p = strip * 16 + r;
   const uint16_t* row = w + (size_t)src_row(p, n, layout) * k;
   const int G = k / kGroup;
-  uint8_t* codes = dst;
-  uint16_t* scales = reinterpret_cast<uint16_t*>(dst + (size_t)n * k / 2);
+  const int Q = strip >> 2, u = strip & 3;
   bool bad = false;
   for (int g = 0; g < G; ++g) {
     float v[32];
@@ -99,10 +100,11 @@ __global__ __launch_bounds__(256) void quant_pack_int4(const uint16_t* __restric
       }
       word[s] = acc;
     }
-    const size_t tile = (size_t)strip * G + g;
-    *reinterpret_cast<uint4*>(codes + tile * 1024 + 16 * lane) =
+    uint8_t* block = dst + ((size_t)Q * G + g) * 4224;
+    *reinterpret_cast<uint4*>(block + 1024 * u + 16 * lane) =
         make_uint4(word[0], word[1], word[2], word[3]);
-    if (c == 0) scales[tile * 16 + r] = __builtin_bit_cast(uint16_t, s16);
+    if (c == 0)
+      *reinterpret_cast<uint16_t*>(block + 4096 + 2 * (4 * r + u)) = __builtin_bit_cast(uint16_t, s16);
   }
   if (bad) atomicOr(err, 1);
 }
@@ -118,6 +120,7 @@ __global__ __launch_bounds__(256) void quant_pack_int8(const uint16_t* __restric
   const int p = strip * 16 + r;
   const uint16_t* row = w + (size_t)src_row(p, n, layout) * k;
   const int G = k / kGroup;
+  const int Q = strip >> 2, u = strip & 3;
   bool bad = false;
   float m = 0.0f;
   for (int g = 0; g < G; ++g) {
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void quant_pack_int8(const uint16_t* __restric
   for (int g = 0; g < G; ++g) {
     float v[32];
     load_lane_group(row, g, c, v, bad);
-    const size_t tile = (size_t)strip * G + g;
+    uint8_t* tile = dst + ((size_t)Q * G + g) * 8192 + 2048 * u;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t word[4];
@@ -147,11 +150,12 @@ __global__ __launch_bounds__(256) void quant_pack_int8(const uint16_t* __restric
         }
         word[j] = acc;
       }
-      *reinterpret_cast<uint4*>(dst + tile * 2048 + 1024 * h + 16 * lane) =
+      *reinterpret_cast<uint4*>(tile + 1024 * h + 16 * lane) =
           make_uint4(word[0], word[1], word[2], word[3]);
     }
   }
-  if (c == 0) reinterpret_cast<uint16_t*>(dst + (size_t)n * k)[p] = __builtin_bit_cast(uint16_t, s16);
+  if (c == 0)
+    reinterpret_cast<uint16_t*>(dst + (size_t)n * k)[64 * Q + 4 * r + u] = __builtin_bit_cast(uint16_t, s16);
   if (bad) atomicOr(err, 1);
 }
 
@@ -165,9 +169,10 @@ __global__ __launch_bounds__(256) void pack_bf16(const uint16_t* __restrict__ w,
   const int p = strip * 16 + r;
   const uint16_t* row = w + (size_t)src_row(p, n, layout) * k;
   const int G = k / kGroup;
+  const int Q = strip >> 2, u = strip & 3;
   bool bad = false;
   for (int g = 0; g < G; ++g) {
-    const size_t tile = (size_t)strip * G + g;
+    uint8_t* tile = dst + ((size_t)Q * G + g) * 16384 + 4096 * u;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4 q = load_u32x4(row + kGroup * g + 32 * s + 8 * c);
@@ -175,8 +180,7 @@ __global__ __launch_bounds__(256) void pack_bf16(const uint16_t* __restrict__ w,
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         bad = bad || bf16_nonfinite(d[j] & 0xffffu) || bf16_nonfinite(d[j] >> 16);
-      *reinterpret_cast<uint4*>(dst + tile * 4096 + 1024 * s + 16 * lane) =
-          make_uint4(q.x, q.y, q.z, q.w);
+      *reinterpret_cast<uint4*>(tile + 1024 * s + 16 * lane) = make_uint4(q.x, q.y, q.z, q.w);
     }
   }
   if (bad) atomicOr(err, 1);

@@ -37,12 +37,12 @@ def test_every_declared_symbol_is_exported():
 def test_packed_size_matches_layout_spec():
     lib = _lib.load()
     for tier in (0, 1, 2):
-        for n, k in [(16, 128), (1536, 2048), (2048, 768), (28672, 4096), (4096, 14336),
-                     (1024, 2048), (64, 256)]:
+        for n, k in [(64, 128), (1536, 2048), (2048, 768), (28672, 4096), (4096, 14336),
+                     (1024, 2048), (192, 256)]:
             assert lib.moe_packed_size(tier, n, k) == oracle.packed_size(tier, n, k)
-    for n, k in [(16, 100), (10, 128), (0, 128), (16, 0), (-16, 128)]:
+    for n, k in [(64, 100), (10, 128), (16, 128), (48, 128), (0, 128), (64, 0), (-64, 128)]:
         assert lib.moe_packed_size(2, n, k) == 0
-    assert lib.moe_packed_size(3, 16, 128) == 0
+    assert lib.moe_packed_size(3, 64, 128) == 0
 
 
 def test_strerror_and_last_error():
@@ -58,16 +58,17 @@ FAKE = 0x100000   # a 256-aligned address that is never dereferenced
 def test_quantize_pack_validation():
     lib = _lib.load()
     q = lib.moe_quantize_pack
-    assert q(5, 0, FAKE, 16, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL      # tier
-    assert q(2, 7, FAKE, 16, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL      # layout
-    assert q(2, 0, None, 16, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL      # null w
-    assert q(2, 0, FAKE, 16, 128, FAKE + 16, 1 << 20, None) == _lib.MOE_EINVAL  # dst align
-    assert q(2, 0, FAKE + 2, 16, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL  # w align
-    assert q(2, 0, FAKE, 16, 100, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE
-    assert q(2, 0, FAKE, 24, 128, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE
-    assert q(2, 1, FAKE, 48, 128, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE     # gate/up needs 64
-    need = lib.moe_packed_size(2, 16, 128)
-    assert q(2, 0, FAKE, 16, 128, FAKE, need - 1, None) == _lib.MOE_ENOSPC
+    assert q(5, 0, FAKE, 64, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL      # tier
+    assert q(2, 7, FAKE, 64, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL      # layout
+    assert q(2, 0, None, 64, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL      # null w
+    assert q(2, 0, FAKE, 64, 128, FAKE + 16, 1 << 20, None) == _lib.MOE_EINVAL  # dst align
+    assert q(2, 0, FAKE + 2, 64, 128, FAKE, 1 << 20, None) == _lib.MOE_EINVAL  # w align
+    assert q(2, 0, FAKE, 64, 100, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE
+    assert q(2, 0, FAKE, 16, 128, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE     # quads of 64 rows
+    assert q(2, 1, FAKE, 48, 128, FAKE, 1 << 20, None) == _lib.MOE_ESHAPE
+    assert q(0, 0, FAKE, 1 << 16, 1 << 15, FAKE, 1 << 40, None) == _lib.MOE_ESHAPE   # >= 4 GiB
+    need = lib.moe_packed_size(2, 64, 128)
+    assert q(2, 0, FAKE, 64, 128, FAKE, need - 1, None) == _lib.MOE_ENOSPC
     assert b"needed" in lib.moe_last_error()
 
 

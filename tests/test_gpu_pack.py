@@ -63,7 +63,7 @@ def test_pack_edge_values(mm):
 
 
 def test_pack_errors(mm):
-    w = np.zeros((16, 128), np.uint16)
+    w = np.zeros((64, 128), np.uint16)
     w[3, 5] = 0x7FC0                                    # NaN
     with pytest.raises(mm.MoeError) as ei:
         mm.quantize_pack(to_dev(w), 2)
@@ -74,3 +74,6 @@ def test_pack_errors(mm):
     assert ei.value.status == 3
     # int8 of the same value is fine (1e6/127 < 65504)
     mm.quantize_pack(to_dev(w), 1)
+    with pytest.raises(mm.MoeError) as ei:      # 16 rows: the layout packs quads of 64
+        mm.quantize_pack(to_dev(w[:16]), 2)
+    assert ei.value.status == 2

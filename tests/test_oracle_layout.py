@@ -21,34 +21,35 @@ def _source_row(p, n, layout):
 
 
 def _coords(p, k, K):
-    """packed row p, column k -> (tile index, lane, step, element)."""
+    """packed row p, column k -> (block index, strip-in-quad, lane, step, element)."""
     G = K // 128
     t, r = divmod(p, 16)
+    Q, u = divmod(t, 4)
     g, kk = divmod(k, 128)
     s, rem = divmod(kk, 32)
     c, i = divmod(rem, 8)
-    return t * G + g, 16 * c + r, s, i
+    return Q * G + g, u, 16 * c + r, s, i
 
 
 def _decode(blob, tier, p, k, N, K):
-    tile, lane, s, i = _coords(p, k, K)
+    block, u, lane, s, i = _coords(p, k, K)
+    r = p % 16
     if tier == TIER_INT4:
-        word_at = tile * 1024 + 16 * lane + 4 * s
+        base = block * 4224
+        word_at = base + 1024 * u + 16 * lane + 4 * s
         word = int.from_bytes(bytes(blob[word_at:word_at + 4]), "little")
         nib = (i // 2) + 4 * (i % 2)
         q = ((word >> (4 * nib)) & 0xF) - 8
-        G = K // 128
-        t, r = divmod(p, 16)
-        sidx = (t * G + k // 128) * 16 + r
-        sa = N * K // 2 + 2 * sidx
+        sa = base + 4096 + 2 * (4 * r + u)
         sc = np.frombuffer(bytes(blob[sa:sa + 2]), dtype="<f2")[0]
         return q, sc
     if tier == TIER_INT8:
-        at = tile * 2048 + (s // 2) * 1024 + 16 * lane + 8 * (s % 2) + i
+        at = block * 8192 + 2048 * u + (s // 2) * 1024 + 16 * lane + 8 * (s % 2) + i
         q = int(blob[at]) - 128
-        sa = N * K + 2 * p
+        Q = p // 64
+        sa = N * K + 2 * (64 * Q + 4 * r + u)
         return q, np.frombuffer(bytes(blob[sa:sa + 2]), dtype="<f2")[0]
-    at = tile * 4096 + s * 1024 + 16 * lane + 2 * i
+    at = block * 16384 + 4096 * u + s * 1024 + 16 * lane + 2 * i
     return int.from_bytes(bytes(blob[at:at + 2]), "little"), None
 
 
@@ -95,9 +96,12 @@ def test_gate_up_interleave_pairs():
 
 
 def test_layout_rejects_bad_shapes():
-    q = np.zeros((16, 100), np.int8)
+    q = np.zeros((64, 100), np.int8)
     with pytest.raises(ValueError):
-        oracle.pack_matrix(TIER_INT8, LAYOUT_PLAIN, q=q, s=np.zeros(16, np.float16))
+        oracle.pack_matrix(TIER_INT8, LAYOUT_PLAIN, q=q, s=np.zeros(64, np.float16))
     q = np.zeros((48, 128), np.int8)
+    with pytest.raises(ValueError):
+        oracle.pack_matrix(TIER_INT8, LAYOUT_PLAIN, q=q, s=np.zeros(48, np.float16))
+    q = np.zeros((96, 128), np.int8)
     with pytest.raises(ValueError):
         oracle.pack_matrix(TIER_INT8, LAYOUT_GATE_UP, q=q, s=np.zeros(48, np.float16))
