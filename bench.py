@@ -239,7 +239,8 @@ def main():
     log("[bench] stage averages (us): " +
         ", ".join(f"{n}={v}" for n, v in zip(STAGES, stage_avg_us)))
 
-    prefill = alg["flops13"] / (alg["bytes13"] / HBM_PEAK_GBS * 1e9) > BF16_PEAK_TFLOPS * 1e12
+    # the kernel is MFMA-bound when its flops take longer at peak than its bytes
+    prefill = alg["flops13"] / (BF16_PEAK_TFLOPS * 1e12) > alg["bytes13"] / (HBM_PEAK_GBS * 1e9)
     g13_s = stage_avg_us[3] * 1e-6
     workload_key = f"cfg{cfg.cid}_T{T}"
     if prefill:

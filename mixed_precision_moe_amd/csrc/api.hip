@@ -61,6 +61,7 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
   w.act = take(sizeof(uint16_t) * R * L.I);
   w.r2 = take(sizeof(float) * R * (L.I / 32));
   w.rows = take(sizeof(float) * R * L.H);
+  w.x16 = take(gp.kind == kGemmPrefill ? sizeof(uint16_t) * T * (size_t)L.H : 0);
   w.total = o;
   return w;
 }
@@ -370,21 +371,37 @@ int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, 
   if (!y || !aligned(y, 16)) return set_error(MOE_EINVAL, "y must be non-null and 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Stages st{L, s, true};
+  const bool prefill = gp.kind == kGemmPrefill;
   hipError_t e = enqueue_route(*L, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
                                at<int32_t>(ws, p.ids), at<float>(ws, p.weights),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
-                               at<int32_t>(ws, p.pos), at<float>(ws, p.r13), ws, st);
+                               at<int32_t>(ws, p.pos), prefill ? nullptr : at<float>(ws, p.r13),
+                               ws, st);
   if (e != hipSuccess) return check_hip(e, "route launch");
   st.rec(3);
-  e = launch_gemm13(*L, gp, T, x, at<int32_t>(ws, p.sorted), at<TileEntry>(ws, p.tiles13),
-                    at<int32_t>(ws, p.ntiles13), p.max_tiles13, at<float>(ws, p.r13),
-                    at<uint16_t>(ws, p.act), at<float>(ws, p.r2), s);
+  if (prefill) {
+    e = launch_x_to_f16(x, at<uint16_t>(ws, p.x16), (size_t)T * L->H, s);
+    if (e == hipSuccess)
+      e = launch_prefill(true, *L, T, at<uint16_t>(ws, p.x16), at<int32_t>(ws, p.sorted),
+                         at<TileEntry>(ws, p.tiles13), at<int32_t>(ws, p.ntiles13), p.max_tiles13,
+                         at<uint16_t>(ws, p.act), nullptr, nullptr, s);
+  } else {
+    e = launch_gemm13(*L, gp, T, x, at<int32_t>(ws, p.sorted), at<TileEntry>(ws, p.tiles13),
+                      at<int32_t>(ws, p.ntiles13), p.max_tiles13, at<float>(ws, p.r13),
+                      at<uint16_t>(ws, p.act), at<float>(ws, p.r2), s);
+  }
   if (e != hipSuccess) return check_hip(e, "gate/up GEMM launch");
   st.rec(4);
-  e = launch_gemm2(*L, gp, T, at<uint16_t>(ws, p.act), at<int32_t>(ws, p.sorted),
-                   at<float>(ws, p.weights), at<TileEntry>(ws, p.tiles2),
-                   at<int32_t>(ws, p.ntiles2), p.max_tiles2, at<float>(ws, p.r2),
-                   at<float>(ws, p.rows), s);
+  if (prefill) {
+    e = launch_prefill(false, *L, T, at<uint16_t>(ws, p.act), at<int32_t>(ws, p.sorted),
+                       at<TileEntry>(ws, p.tiles2), at<int32_t>(ws, p.ntiles2), p.max_tiles2,
+                       nullptr, at<float>(ws, p.weights), at<float>(ws, p.rows), s);
+  } else {
+    e = launch_gemm2(*L, gp, T, at<uint16_t>(ws, p.act), at<int32_t>(ws, p.sorted),
+                     at<float>(ws, p.weights), at<TileEntry>(ws, p.tiles2),
+                     at<int32_t>(ws, p.ntiles2), p.max_tiles2, at<float>(ws, p.r2),
+                     at<float>(ws, p.rows), s);
+  }
   if (e != hipSuccess) return check_hip(e, "down GEMM launch");
   st.rec(5);
   e = launch_combine(at<float>(ws, p.rows), at<int32_t>(ws, p.pos), T, L->H, L->k, y, y_dtype, s);

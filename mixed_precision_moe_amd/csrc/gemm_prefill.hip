@@ -1,0 +1,415 @@
+// gemm_prefill.hip -- large-batch grouped expert GEMMs (MFMA-bound regime).
+//
+// "Every Expert Counts: ExactMoE ..." §3.4: one fused gate/up grouped GEMM and
+// one down grouped GEMM over the whole token matrix; §5.4 (Table 4): more
+// routes coalesced per expert turn the grouped kernel from weight streaming
+// into arithmetic.  Weights are dequantized in registers, never materialized
+// as a full fp16 matrix (§3.1, §3.3); as in the MARLIN kernel the pages use,
+// the dequantized weight q*s is rounded once to fp16 (relative error at most
+// 2^-12) and the product runs on fp16 MFMA with fp32 accumulation.
+// Activations enter as fp16 re-encodings of their bf16 values (exact for
+// magnitudes in [2^-14, 65504]; larger magnitudes saturate to +-65504).
+//
+// Block: 256 threads (2 x 2 waves), tile 256 rows x 256 columns of one expert,
+// K staged in chunks of 64 through double-buffered LDS.  Per chunk the whole
+// block cooperatively loads the activation rows (gathered through the grouped
+// route order) and the packed weights of its 256 columns, dequantizes the
+// weights (one thread per column and strip row) and writes both as fp16 row
+// panels; each wave then runs 8 x 8 v_mfma_f32_16x16x32_f16 tiles (128 x 128)
+// per 32-wide k-step with accumulators in AGPRs.
+#include <type_traits>
+
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short f16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
+
+constexpr int PBM = 256, PBN = 256, PBK = 64;
+constexpr int PLD = PBK + 8;           // LDS row stride in halves (144 B: conflict-free reads)
+constexpr int kPrefillThreads = 256;
+constexpr size_t kPrefillLds = (size_t)2 * 2 * PBM * PLD * sizeof(uint16_t);   // 147456 B
+
+struct PrefillArgs {
+  const DevHandle* table;
+  const TileEntry* tiles;
+  const int32_t* ntiles;
+  int max_tiles;
+  const uint16_t* a16;       // fp16 activations: gate/up x16 [T, H]; down act16 [T*k, I]
+  uint32_t a16_bytes;        // size of that array
+  const int32_t* sorted;
+  int top_k;
+  int K, N;
+  uint16_t* act16;           // gate/up output [T*k, I] fp16 (bf16-rounded values)
+  int I;
+  const float* topk_w;       // down epilogue
+  float* rows;               // [T*k, H]
+};
+
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+// fp16 magic: 0x6400 | u is the fp16 value 1024 + u for u < 1024.
+__device__ __forceinline__ void dequant_int4_word(uint32_t w, half2_t s2, uint32_t out[4]) {
+  const uint32_t mask = 0x000f000fu, magic = 0x64006400u;
+  const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = ((w >> (4 * j)) & mask) | magic;     // elements 2j, 2j+1
+    const half2_t q = as_h2(t) + bias;                       // exact: q in [-8, 7]
+    out[j] = as_u32(q * s2);                                 // fp16(q * s)
+  }
+}
+
+__device__ __forceinline__ void dequant_int8_word(uint32_t w, half2_t s2, uint32_t& lo, uint32_t& hi) {
+  const uint32_t mask = 0x00ff00ffu, magic = 0x64006400u;
+  const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t t02 = as_u32((as_h2((w & mask) | magic) + bias) * s2);          // e0, e2
+  const uint32_t t13 = as_u32((as_h2(((w >> 8) & mask) | magic) + bias) * s2);   // e1, e3
+  lo = __builtin_amdgcn_perm(t13, t02, 0x05040100u);   // (e0, e1)
+  hi = __builtin_amdgcn_perm(t13, t02, 0x07060302u);   // (e2, e3)
+}
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(fminf(fmaxf(lo, -65504.f), 65504.f),
+                                                                fminf(fmaxf(hi, -65504.f), 65504.f)));
+}
+
+template <int TIER>
+struct PTier;
+template <>
+struct PTier<MOE_TIER_INT4> { static constexpr int kBlock = 4224; };
+template <>
+struct PTier<MOE_TIER_INT8> { static constexpr int kBlock = 8192; };
+template <>
+struct PTier<MOE_TIER_BF16> { static constexpr int kBlock = 16384; };
+
+template <int TIER>
+__device__ __forceinline__ uint32_t payload_bytes(int N, int K) {
+  if constexpr (TIER == MOE_TIER_INT4) return (uint32_t)(N / 64) * (K / kGroup) * 4224u;
+  else if constexpr (TIER == MOE_TIER_INT8) return (uint32_t)N * K + 2u * N;
+  else return 2u * N * K;
+}
+
+// Weight staging role of one thread: column r of strip `strip` (16 strips of
+// the block), all 64 k of the chunk.  Raw registers hold what the chunk needs:
+// int4 4 x 8 B (chunk c = 0..3, two k-steps each), int8 4 x 16 B, bf16 8 x 16 B.
+template <int TIER>
+struct BRaw;
+template <>
+struct BRaw<MOE_TIER_INT4> { uint2 w[4]; uint32_t scale; };
+template <>
+struct BRaw<MOE_TIER_INT8> { u32x4 w[4]; };
+template <>
+struct BRaw<MOE_TIER_BF16> { u32x4 w[8]; };
+
+// voff: this thread's byte offset inside the block's first quad row of blocks
+// (its quad within the block times G blocks, plus the strip and column
+// position); soff: the block-uniform offset of k-group g of the block's first
+// quad.  Everything thread-dependent is in voff, so the loads need no
+// per-lane scalar values.
+template <int TIER>
+__device__ __forceinline__ void load_b_chunk(BRaw<TIER>& raw, __amdgpu_buffer_rsrc_t rsrc,
+                                             uint32_t voff, uint32_t soff, int h) {
+  if constexpr (TIER == MOE_TIER_INT4) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw.w[c] = buffer_load8(rsrc, voff + 256 * c + 8 * h, soff);
+  } else if constexpr (TIER == MOE_TIER_INT8) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw.w[c] = buffer_load16<true>(rsrc, voff + 1024 * h + 256 * c, soff);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        raw.w[2 * c + s2] = buffer_load16<true>(rsrc, voff + 1024 * (2 * h + s2) + 256 * c, soff);
+  }
+}
+
+// Dequantize the thread's raw chunk and write its column (64 fp16) to LDS.
+// Within the chunk, k-step ks (0, 1) and chunk c hold k = 32 ks + 8 c + i.
+template <int TIER>
+__device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale,
+                                              uint16_t* brow) {
+  if constexpr (TIER == MOE_TIER_INT4) {
+    const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)raw.scale);
+    const half2_t s2 = {sh, sh};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t o0[4], o1[4];
+      dequant_int4_word(raw.w[c].x, s2, o0);     // k-step 0 of the chunk
+      dequant_int4_word(raw.w[c].y, s2, o1);     // k-step 1
+      *reinterpret_cast<uint4*>(brow + 8 * c) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint4*>(brow + 32 + 8 * c) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    }
+  } else if constexpr (TIER == MOE_TIER_INT8) {
+    const _Float16 sh = (_Float16)row_scale;
+    const half2_t s2 = {sh, sh};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
+      dequant_int8_word(raw.w[c].x, s2, a0, a1);   // k-step 0, elements 0..3
+      dequant_int8_word(raw.w[c].y, s2, b0, b1);   // k-step 0, elements 4..7
+      dequant_int8_word(raw.w[c].z, s2, c0, c1);   // k-step 1, elements 0..3
+      dequant_int8_word(raw.w[c].w, s2, d0, d1);   // k-step 1, elements 4..7
+      *reinterpret_cast<uint4*>(brow + 8 * c) = make_uint4(a0, a1, b0, b1);
+      *reinterpret_cast<uint4*>(brow + 32 + 8 * c) = make_uint4(c0, c1, d0, d1);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const u32x4 v = raw.w[2 * c + s2];
+        *reinterpret_cast<uint4*>(brow + 32 * s2 + 8 * c) =
+            make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+                       bf16x2_to_f16x2(v.w));
+      }
+  }
+}
+
+typedef _Float16 f16x8v_t __attribute__((__vector_size__(8 * sizeof(_Float16))));
+
+__device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v_t, a),
+                                                __builtin_bit_cast(f16x8v_t, b), c, 0, 0, 0);
+}
+
+template <int TIER, bool GATE_UP>
+__device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uint8_t* blob,
+                                                 const int (&arow)[8], int n_block,
+                                                 uint16_t* lds, f32x4_t (&acc)[8][8]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = a.K, G = K / kGroup, KC = K / PBK;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<TIER>(a.N, K));
+  // weight staging role: strip (tid >> 4: 0..15 in the block), column r
+  const int qloc = tid >> 6, u = (tid >> 4) & 3, r = tid & 15;
+  const int quad0 = n_block / 64;                       // block-uniform
+  constexpr int kBlk = PTier<TIER>::kBlock;
+  uint32_t bvoff;
+  if constexpr (TIER == MOE_TIER_INT4)
+    bvoff = (uint32_t)qloc * G * kBlk + 1024u * u + 16u * r;   // + 256 c + 8 h; scale: see below
+  else if constexpr (TIER == MOE_TIER_INT8)
+    bvoff = (uint32_t)qloc * G * kBlk + 2048u * u + 16u * r;
+  else
+    bvoff = (uint32_t)qloc * G * kBlk + 4096u * u + 16u * r;
+  // int4 scale of (column r, strip u) within the block's scale area
+  const uint32_t svoff = (uint32_t)qloc * G * kBlk + 2u * (4 * r + u);
+  float row_scale = 0.0f;
+  if constexpr (TIER == MOE_TIER_INT8)
+    row_scale = (float)__builtin_bit_cast(
+        _Float16, buffer_load_u16(rsrc, 2 * (64 * qloc + 4 * r + u), (uint32_t)a.N * K + 128u * quad0));
+  // activation staging role: 8 (row, 16-byte column) chunks per thread
+  const int acol = 8 * (tid & 7);
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a.a16, a.a16_bytes);
+  uint32_t avoff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) avoff[q] = (uint32_t)arow[q] * K * 2u + 2u * acol;
+
+  uint16_t* As[2] = {lds, lds + PBM * PLD};
+  uint16_t* Bs[2] = {lds + 2 * PBM * PLD, lds + 3 * PBM * PLD};
+
+  BRaw<TIER> braw;
+  u32x4 araw[8];
+  auto load_chunk = [&](int kc) {
+    const uint32_t soff = (uint32_t)(quad0 * G + (kc >> 1)) * kBlk;
+    load_b_chunk<TIER>(braw, rsrc, bvoff, soff, kc & 1);
+    if constexpr (TIER == MOE_TIER_INT4) braw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) araw[q] = buffer_load16<false>(arsrc, avoff[q], 2u * PBK * kc);
+  };
+  auto store_chunk = [&](int buf) {
+    store_b_chunk<TIER>(braw, row_scale, Bs[buf] + (16 * (tid >> 4) + r) * PLD);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      *reinterpret_cast<uint4*>(As[buf] + ((tid >> 3) + 32 * q) * PLD + acol) =
+          make_uint4(araw[q].x, araw[q].y, araw[q].z, araw[q].w);
+  };
+
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  for (int kc = 0; kc < KC; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < KC) load_chunk(kc + 1);
+    const uint16_t* Aw = As[buf] + (128 * wm + fr) * PLD + fk;
+    const uint16_t* Bw = Bs[buf] + (128 * wn + fr) * PLD + fk;
+#pragma nounroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8_t af[8], bf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[i] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(Aw + 16 * i * PLD + 32 * ks));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        bf[j] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(Bw + 16 * j * PLD + 32 * ks));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_f16(af[i], bf[j], acc[i][j]);
+    }
+    if (kc + 1 < KC) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_as_f16(float v) {
+  // round to bf16 (the activation precision of the layer), then re-encode as fp16
+  const float b = __uint_as_float(f32_to_bf16_rne(v) << 16);
+  const float c = fminf(fmaxf(b, -65504.f), 65504.f);
+  return __builtin_bit_cast(uint16_t, (_Float16)c);
+}
+
+// One tile of one tier: accumulate, then the epilogue (SwiGLU -> fp16
+// activations for gate/up; routing weight -> fp32 rows for down).
+template <int TIER, bool GATE_UP>
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEntry& te,
+                                             const uint8_t* blob, const int (&arow)[8],
+                                             int n_block, uint16_t* plds) {
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  prefill_mainloop<TIER, GATE_UP>(a, blob, arow, n_block, plds, acc);
+  const int col0 = n_block + 128 * wn;     // first packed column of this wave
+  if constexpr (GATE_UP) {
+    // tiles 4q+0,1 are gate, 4q+2,3 the matching up columns of quad (col0/64 + q)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int icol = 32 * (col0 / 64 + q) + 16 * half + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
+            if (m < te.rows) {
+              const float g = acc[i][4 * q + half][e], up = acc[i][4 * q + half + 2][e];
+              a.act16[(size_t)(te.row_start + m) * a.I + icol] = f32_to_bf16_as_f16(silu_f32(g) * up);
+            }
+          }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
+        if (m < te.rows) {
+          const int pos = te.row_start + m;
+          const float wgt = a.topk_w[a.sorted[pos]];
+          float* out = a.rows + (size_t)pos * a.N + col0 + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) out[16 * j] = wgt * acc[i][j][e];
+        }
+      }
+  }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t plds[];
+  // Column blocks of one M-tile are adjacent in launch order, so the blocks
+  // sharing an activation tile run together (it is read from HBM about once),
+  // and consecutive M-tiles of an expert reuse its weights from the last-level
+  // cache.
+  const int n_blocks = a.N / PBN;
+  const int tile_idx = blockIdx.x / n_blocks;
+  const int nb = blockIdx.x - tile_idx * n_blocks;
+  if (tile_idx >= uniform(*a.ntiles)) return;
+  TileEntry te = a.tiles[tile_idx];
+  te.expert = uniform(te.expert);
+  te.row_start = uniform(te.row_start);
+  te.rows = uniform(te.rows);
+  DevHandle h = a.table[te.expert];
+  h.tier = uniform(h.tier);
+  h.w13 = uniform_ptr(h.w13);
+  h.w2 = uniform_ptr(h.w2);
+  const int tid = threadIdx.x;
+  const int n_block = nb * PBN;
+
+  // activation rows this thread stages (row (tid >> 3) + 32 q); rows past the
+  // tile's count read the tile's last row (their results are never stored)
+  int arow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int m = min((tid >> 3) + 32 * q, te.rows - 1);
+    const int pos = te.row_start + m;
+    arow[q] = GATE_UP ? a.sorted[pos] / a.top_k : pos;
+  }
+
+  const uint8_t* blob = GATE_UP ? h.w13 : h.w2;
+  switch (h.tier) {
+    case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP>(a, te, blob, arow, n_block, plds); break;
+    case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP>(a, te, blob, arow, n_block, plds); break;
+    default: prefill_body<MOE_TIER_BF16, GATE_UP>(a, te, blob, arow, n_block, plds); break;
+  }
+}
+
+// x (bf16) -> fp16 re-encoding for the large-batch path (exact in fp16's
+// normal range, saturating beyond it).  8 elements per thread.
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x,
+                                                       uint16_t* __restrict__ x16, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+  reinterpret_cast<uint4*>(x16)[i] =
+      make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+}
+
+}  // namespace
+
+size_t prefill_lds_bytes() { return kPrefillLds; }
+
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream_t s) {
+  const size_t n8 = n / 8;
+  hipLaunchKernelGGL(x_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, x16, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
+                          const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
+                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s) {
+  PrefillArgs a{};
+  a.table = L.table;
+  a.tiles = tiles;
+  a.ntiles = ntiles;
+  a.max_tiles = max_tiles;
+  a.a16 = a16;
+  a.a16_bytes = (uint32_t)((gate_up ? (size_t)T * L.H : (size_t)T * L.k * L.I) * 2);
+  a.sorted = sorted;
+  a.top_k = L.k;
+  a.K = gate_up ? L.H : L.I;
+  a.N = gate_up ? 2 * L.I : L.H;
+  a.act16 = act16;
+  a.I = L.I;
+  a.topk_w = topk_w;
+  a.rows = rows;
+  static bool attr[2] = {false, false};
+  const void* kern = gate_up ? reinterpret_cast<const void*>(gemm_prefill_kernel<true>)
+                             : reinterpret_cast<const void*>(gemm_prefill_kernel<false>);
+  if (!attr[gate_up]) {
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)kPrefillLds);
+    if (e != hipSuccess) return e;
+    attr[gate_up] = true;
+  }
+  const dim3 grid((unsigned)((a.N / PBN) * max_tiles));
+  if (gate_up)
+    hipLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPrefillThreads), kPrefillLds, s, a);
+  else
+    hipLaunchKernelGGL(gemm_prefill_kernel<false>, grid, dim3(kPrefillThreads), kPrefillLds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -650,9 +650,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
   const double rows_per_expert = (double)T * L.k / L.E;
-  const bool decode = rows_per_expert <= 4.0;
-  p.kind = decode ? 1 : 0;
-  p.bm13 = decode ? kDecodeRows : 64;
+  const bool decode = rows_per_expert <= (double)kDecodeRows;
+  p.kind = decode ? kGemmDecode : kGemmPrefill;
+  p.bm13 = decode ? kDecodeRows : 256;
   p.bm2 = p.bm13;
   return p;
 }
@@ -675,7 +675,7 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.act = act;
   a.r2 = r2;
   a.I = L.I;
-  if (gp.kind == 1) return launch_decode<4, true>(a, max_tiles, s);
+  if (gp.kind == kGemmDecode) return launch_decode<4, true>(a, max_tiles, s);
   return launch_gg<4, true>(a, max_tiles, s);
 }
 
@@ -696,7 +696,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.N = L.H;
   a.topk_w = topk_w;
   a.rows = rows;
-  if (gp.kind == 1) return launch_decode<4, false>(a, max_tiles, s);
+  if (gp.kind == kGemmDecode) return launch_decode<4, false>(a, max_tiles, s);
   return launch_gg<4, false>(a, max_tiles, s);
 }
 

@@ -32,17 +32,20 @@ struct TileEntry {
   int32_t pad;
 };
 
-// Tile size choices for one forward, picked on the host from T and the layer.
+// Kernel family and M-tile size for one forward, picked on the host from T
+// and the layer: decode (few routes per expert, weight streaming, exact
+// integer MFMA operands) or prefill (many routes per expert, fp16 MFMA).
+enum GemmKind { kGemmDecode = 1, kGemmPrefill = 2 };
 struct GemmPlan {
   int bm13;   // rows per M-tile, gate/up GEMM
   int bm2;    // rows per M-tile, down GEMM
-  int kind;   // kernel family (see grouped_gemm.hip)
+  int kind;   // GemmKind
 };
 
 // Byte offsets of the workspace regions for T tokens.
 struct WsPlan {
   size_t logits, ids, weights, offsets, sorted, pos, tiles13, ntiles13, tiles2, ntiles2;
-  size_t r13, act, r2, rows;
+  size_t r13, act, r2, rows, x16;
   size_t total;
   int max_tiles13, max_tiles2;
 };
@@ -83,6 +86,11 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
                         const int32_t* sorted, const float* topk_w, const TileEntry* tiles,
                         const int32_t* ntiles, int max_tiles, const float* r2, float* rows,
                         hipStream_t s);
+size_t prefill_lds_bytes();
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream_t s);
+hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
+                          const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
+                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s);
 hipError_t launch_combine(const float* rows, const int32_t* pos, int T, int H, int k, void* y,
                           int y_dtype, hipStream_t s);
 
