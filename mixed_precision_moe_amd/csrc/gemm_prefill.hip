@@ -26,6 +26,11 @@ namespace moe {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+// LDS pointers with their address space spelled out, so every access is a
+// ds_read / ds_write (a generic pointer would become a flat access).
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) v4u32 lds_u4;
 typedef short f16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 
 constexpr int PBM = 256, PBN = 256, PBK = 64;
@@ -134,7 +139,7 @@ __device__ __forceinline__ void load_b_chunk(BRaw<TIER>& raw, __amdgpu_buffer_rs
 // Within the chunk, k-step ks (0, 1) and chunk c hold k = 32 ks + 8 c + i.
 template <int TIER>
 __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale,
-                                              uint16_t* brow) {
+                                              lds_u16* brow) {
   if constexpr (TIER == MOE_TIER_INT4) {
     const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)raw.scale);
     const half2_t s2 = {sh, sh};
@@ -143,8 +148,8 @@ __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_s
       uint32_t o0[4], o1[4];
       dequant_int4_word(raw.w[c].x, s2, o0);     // k-step 0 of the chunk
       dequant_int4_word(raw.w[c].y, s2, o1);     // k-step 1
-      *reinterpret_cast<uint4*>(brow + 8 * c) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-      *reinterpret_cast<uint4*>(brow + 32 + 8 * c) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      *reinterpret_cast<lds_u4*>(brow + 8 * c) = v4u32{o0[0], o0[1], o0[2], o0[3]};
+      *reinterpret_cast<lds_u4*>(brow + 32 + 8 * c) = v4u32{o1[0], o1[1], o1[2], o1[3]};
     }
   } else if constexpr (TIER == MOE_TIER_INT8) {
     const _Float16 sh = (_Float16)row_scale;
@@ -156,8 +161,8 @@ __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_s
       dequant_int8_word(raw.w[c].y, s2, b0, b1);   // k-step 0, elements 4..7
       dequant_int8_word(raw.w[c].z, s2, c0, c1);   // k-step 1, elements 0..3
       dequant_int8_word(raw.w[c].w, s2, d0, d1);   // k-step 1, elements 4..7
-      *reinterpret_cast<uint4*>(brow + 8 * c) = make_uint4(a0, a1, b0, b1);
-      *reinterpret_cast<uint4*>(brow + 32 + 8 * c) = make_uint4(c0, c1, d0, d1);
+      *reinterpret_cast<lds_u4*>(brow + 8 * c) = v4u32{a0, a1, b0, b1};
+      *reinterpret_cast<lds_u4*>(brow + 32 + 8 * c) = v4u32{c0, c1, d0, d1};
     }
   } else {
 #pragma unroll
@@ -165,9 +170,9 @@ __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_s
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const u32x4 v = raw.w[2 * c + s2];
-        *reinterpret_cast<uint4*>(brow + 32 * s2 + 8 * c) =
-            make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
-                       bf16x2_to_f16x2(v.w));
+        *reinterpret_cast<lds_u4*>(brow + 32 * s2 + 8 * c) =
+            v4u32{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+                  bf16x2_to_f16x2(v.w)};
       }
   }
 }
@@ -182,7 +187,7 @@ __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uint8_t* blob,
                                                  const int (&arow)[8], int n_block,
-                                                 uint16_t* lds, f32x4_t (&acc)[8][8]) {
+                                                 lds_u16* lds, f32x4_t (&acc)[8][8]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K, G = K / kGroup, KC = K / PBK;
@@ -211,8 +216,9 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
 #pragma unroll
   for (int q = 0; q < 8; ++q) avoff[q] = (uint32_t)arow[q] * K * 2u + 2u * acol;
 
-  uint16_t* As[2] = {lds, lds + PBM * PLD};
-  uint16_t* Bs[2] = {lds + 2 * PBM * PLD, lds + 3 * PBM * PLD};
+  // LDS: A buffers at 0 and PBM*PLD, B buffers at 2*PBM*PLD and 3*PBM*PLD
+  auto As = [&](int buf) { return lds + buf * (PBM * PLD); };
+  auto Bs = [&](int buf) { return lds + (2 + buf) * (PBM * PLD); };
 
   BRaw<TIER> braw;
   u32x4 araw[8];
@@ -224,36 +230,44 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
     for (int q = 0; q < 8; ++q) araw[q] = buffer_load16<false>(arsrc, avoff[q], 2u * PBK * kc);
   };
   auto store_chunk = [&](int buf) {
-    store_b_chunk<TIER>(braw, row_scale, Bs[buf] + (16 * (tid >> 4) + r) * PLD);
+    store_b_chunk<TIER>(braw, row_scale, Bs(buf) + (16 * (tid >> 4) + r) * PLD);
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      *reinterpret_cast<uint4*>(As[buf] + ((tid >> 3) + 32 * q) * PLD + acol) =
-          make_uint4(araw[q].x, araw[q].y, araw[q].z, araw[q].w);
+      *reinterpret_cast<lds_u4*>(As(buf) + ((tid >> 3) + 32 * q) * PLD + acol) =
+          v4u32{araw[q].x, araw[q].y, araw[q].z, araw[q].w};
+  };
+
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  f16x8_t fa0[8], fb0[8];
+  auto read_frags = [&](int buf, int ks, f16x8_t (&fa)[8], f16x8_t (&fb)[8]) {
+    const lds_u16* Aw = As(buf) + (128 * wm + fr) * PLD + fk + 32 * ks;
+    const lds_u16* Bw = Bs(buf) + (128 * wn + fr) * PLD + fk + 32 * ks;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      fa[i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + 16 * i * PLD));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      fb[j] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Bw + 16 * j * PLD));
+  };
+  auto mfma_block = [&](const f16x8_t (&fa)[8], const f16x8_t (&fb)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mfma_f16(fa[i], fb[j], acc[i][j]);
   };
 
   load_chunk(0);
   store_chunk(0);
   __syncthreads();
-  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  // chunk kc+1 is loaded from memory while chunk kc is multiplied, then
+  // dequantized into the other LDS buffer
   for (int kc = 0; kc < KC; ++kc) {
     const int buf = kc & 1;
     if (kc + 1 < KC) load_chunk(kc + 1);
-    const uint16_t* Aw = As[buf] + (128 * wm + fr) * PLD + fk;
-    const uint16_t* Bw = Bs[buf] + (128 * wn + fr) * PLD + fk;
-#pragma nounroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8_t af[8], bf[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[i] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(Aw + 16 * i * PLD + 32 * ks));
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bf[j] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(Bw + 16 * j * PLD + 32 * ks));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_f16(af[i], bf[j], acc[i][j]);
-    }
+    read_frags(buf, 0, fa0, fb0);
+    mfma_block(fa0, fb0);
+    read_frags(buf, 1, fa0, fb0);
+    mfma_block(fa0, fb0);
     if (kc + 1 < KC) store_chunk(buf ^ 1);
     __syncthreads();
   }
@@ -271,7 +285,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_as_f16(float v) {
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEntry& te,
                                              const uint8_t* blob, const int (&arow)[8],
-                                             int n_block, uint16_t* plds) {
+                                             int n_block, lds_u16* plds) {
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   f32x4_t acc[8][8];
@@ -349,10 +363,11 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
   }
 
   const uint8_t* blob = GATE_UP ? h.w13 : h.w2;
+  lds_u16* lds = (lds_u16*)plds;
   switch (h.tier) {
-    case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP>(a, te, blob, arow, n_block, plds); break;
-    case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP>(a, te, blob, arow, n_block, plds); break;
-    default: prefill_body<MOE_TIER_BF16, GATE_UP>(a, te, blob, arow, n_block, plds); break;
+    case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP>(a, te, blob, arow, n_block, lds); break;
+    case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP>(a, te, blob, arow, n_block, lds); break;
+    default: prefill_body<MOE_TIER_BF16, GATE_UP>(a, te, blob, arow, n_block, lds); break;
   }
 }
 
