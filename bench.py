@@ -36,7 +36,10 @@ METRIC = "MoE-layer tokens/s; % HBM roofline (decode) and % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 STAGES = ["route_logits", "topk", "grouping", "gemm_gate_up_swiglu", "gemm_down", "combine"]
-KERNEL_SOURCE = os.path.join(ROOT, "mixed_precision_moe_amd", "csrc", "grouped_gemm.hip")
+CSRC = os.path.join(ROOT, "mixed_precision_moe_amd", "csrc")
+# sources of the dominant kernel of each path (a change voids stored counters)
+KERNEL_SOURCES = {"decode": ("grouped_gemm.hip", "device_util.h"),
+                  "prefill": ("gemm_prefill.hip", "device_util.h")}
 
 
 def log(msg):
@@ -51,9 +54,12 @@ def packed_bytes(tier, n, k):
     return 2 * n * k
 
 
-def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(path_kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[path_kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def build_layers(cfg, tiers, R, dev):
@@ -136,9 +142,10 @@ def cpu_baseline(cfg, tiers, x, wr, bias, min_seconds=10.0, max_seconds=30.0):
             "seconds": round(el, 2)}
 
 
-def stored_traffic(workload_key):
+def stored_traffic(workload_key, path_kind):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    counter runs, if they were taken on the current kernel source."""
+    counter runs (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
+    size), if they were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
@@ -146,7 +153,7 @@ def stored_traffic(workload_key):
         d = json.load(open(path)).get(workload_key)
     except (ValueError, OSError):
         return None
-    if not d or d.get("source_sha") != source_hash():
+    if not d or d.get("source_sha") != source_hash(path_kind):
         return None
     return d.get("traffic_bytes")
 
@@ -254,7 +261,7 @@ def main():
     roof["kernel"] = "grouped_gemm gate/up + SwiGLU"
     roof["avg_launch_us"] = float(stage_avg_us[3])
     roof["algorithmic_per_launch"] = alg["flops13"] if prefill else alg["bytes13"]
-    roof["traffic"] = stored_traffic(workload_key)
+    roof["traffic"] = stored_traffic(workload_key, "prefill" if prefill else "decode")
 
     layer_roof_s = max(alg["bytes_layer"] / (HBM_PEAK_GBS * 1e9),
                        alg["flops_layer"] / (BF16_PEAK_TFLOPS * 1e12))
