@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=None, help="weight-set copies (default: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each forward from the host instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run plain device copies of this many MiB (for scaling HBM "
                          "counters) and exit")
@@ -190,7 +192,15 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"[bench] copied {n} bytes x 3 (read {n}, write {n} per copy)")
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / 10
+        log(f"[bench] copied {n} bytes x 13 (read {n}, write {n} per copy); "
+            f"{ms * 1e3:.1f} us per copy = {2 * n / ms / 1e6:.0f} GB/s read+write")
         return
     cfg = inputs.get_config(args.config)
     T = cfg.default_tokens if args.tokens is None else args.tokens
@@ -223,23 +233,42 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # Timed region 1: one host launch per forward, HIP events recorded on the
+    # forward's stream around every stage (the per-kernel durations).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i in range(K):                     # create the events before the timed region
         for e in ev[i]:
             e.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        L = layers[i % R]
-        L.set_stage_events(ev[i])
+        layers[i % R].set_stage_events(ev[i])
         fwd[i % R]()
     end.record(stream)
     torch.cuda.synchronize()
     for L in layers:
         L.set_stage_events(None)
-    total_ms = start.elapsed_time(end)
+    eager_ms = start.elapsed_time(end)
     stage_ms = np.array([[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(6)] for i in range(K)])
+    total_ms, launch = eager_ms, "host launch per forward"
+    if not args.eager:
+        # Timed region 2: one HIP graph holds R forwards (one per weight copy);
+        # the region replays it back to back.  Throughput is taken from here.
+        K = max(R, (K // R) * R)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for r in range(R):
+                layers[r].bind_forward(x, wr, bias, y, workspace=ws, stream=cap)()
+        graph.replay()                     # one untimed replay
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(K // R):
+            graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        total_ms, launch = start.elapsed_time(end), f"HIP graph of {R} forwards, replayed"
     stage_avg_us = (stage_ms.mean(axis=0) * 1000).round(2)
     ms_per_step = total_ms / K
     value = T * K / (total_ms / 1000.0)
@@ -283,6 +312,7 @@ def main():
             "tokens": T, "hidden": cfg.hidden, "experts": cfg.n_experts, "top_k": cfg.top_k,
             "inter": cfg.inter, "touched_experts": alg["touched"],
             "weight_copies_rotated": R, "output": args.out_dtype,
+            "launch": launch, "ms_per_step_host_launch": round(eager_ms / args.steps, 4),
             "layer_roofline_frac": round(layer_roof_s / (ms_per_step / 1000.0), 4),
             "stage_avg_us": dict(zip(STAGES, [float(v) for v in stage_avg_us])),
         },

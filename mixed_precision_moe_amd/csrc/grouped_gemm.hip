@@ -394,6 +394,8 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
 // from LDS (rows beyond the tile's count are zero and never read).  For a
 // gate/up matrix NS = 4 covers 32 gate and the matching 32 up columns.
 // ---------------------------------------------------------------------------
+// s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 constexpr int kDecodeRows = 8;   // rows of an M-tile in the decode kernel (MFMA rows 8..15 are zero)
 constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
 
@@ -450,6 +452,11 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
       }
     }
   }
+  // Drain every load before the barrier.  The staging loops above are skipped
+  // by waves without work; on that path the first weight loads would still be
+  // pending at the main loop, and the compiler's merged wait state then drains
+  // all loads at the top of every iteration instead of only the oldest group.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   float row_scale[NS];
@@ -458,52 +465,73 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, ns);
   }
-  const bool arow_ok = (lane & 15) < rows;
-  const uint16_t* la = lds_a + (lane & 15) * lda + 8 * (lane >> 4);
+  // A fragments: lane l reads LDS row l % 8.  MFMA rows 8..15 (and rows at or
+  // beyond the tile's count) then hold copies or stale data; they only feed
+  // accumulator rows that the epilogue never stores, so no lane is masked.
+  const uint16_t* la = lds_a + (lane & 7) * lda + 8 * (lane >> 4);
 
+  auto consume = [&](int g, int d) {
+    f32x4_t p[NS];
+    if constexpr (TIER == MOE_TIER_BF16) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) p[ns] = acc[ns];
+    } else {
+      const float4 r4 = *reinterpret_cast<const float4*>(lds_r + g * kRStride + 4 * (lane >> 4));
+      const f32x4_t init = {-TR::kOffset * r4.x, -TR::kOffset * r4.y, -TR::kOffset * r4.z,
+                            -TR::kOffset * r4.w};
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) p[ns] = init;
+    }
+    bf16x8_t af[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) af[s4] = as_bf16x8(load_u32x4(la + kGroup * g + 32 * s4));
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) p[ns] = mfma16x16x32(af[s4], b_operand<TIER>(bb[d][ns], s4, c4), p[ns]);
+    if constexpr (TIER == MOE_TIER_BF16) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) acc[ns] = p[ns];
+    } else {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        float scf;
+        if constexpr (TIER == MOE_TIER_INT4)
+          scf = half_of(sc[d], ns);
+        else
+          scf = row_scale[ns];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(scf, p[ns][i], acc[ns][i]);
+      }
+    }
+  };
+
+  // Steady state: every group consumed here has a successor D groups ahead, so
+  // the body is branch-free and each register set bb[d] keeps its role (no
+  // copies between loads in flight, which would force early waits).
+  int g0 = 0;
 #pragma nounroll
-  for (int g0 = 0; g0 < G; g0 += D) {
+  for (; g0 + 2 * D <= G; g0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int g = g0 + d;
-      if (g >= G) break;
-      f32x4_t p[NS];
-      if constexpr (TIER == MOE_TIER_BF16) {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) p[ns] = acc[ns];
-      } else {
-        const float4 r4 = *reinterpret_cast<const float4*>(lds_r + g * kRStride + 4 * (lane >> 4));
-        const f32x4_t init = {-TR::kOffset * r4.x, -TR::kOffset * r4.y, -TR::kOffset * r4.z,
-                              -TR::kOffset * r4.w};
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) p[ns] = init;
-      }
-      bf16x8_t af[4];
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        af[s4] = as_bf16x8(arow_ok ? load_u32x4(la + kGroup * g + 32 * s4) : u32x4{0, 0, 0, 0});
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) p[ns] = mfma16x16x32(af[s4], b_operand<TIER>(bb[d][ns], s4, c4), p[ns]);
-      if constexpr (TIER == MOE_TIER_BF16) {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) acc[ns] = p[ns];
-      } else {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-          float scf;
-          if constexpr (TIER == MOE_TIER_INT4)
-            scf = half_of(sc[d], ns);
-          else
-            scf = row_scale[ns];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(scf, p[ns][i], acc[ns][i]);
-        }
-      }
-      if (g + D < G) issue(g + D, d);
+      consume(g0 + d, d);
+      issue(g0 + d + D, d);
+      // keep the next group's math after this reload: otherwise the scheduler
+      // batches the math of all D groups ahead of every reload and the wave
+      // computes with no weight loads in flight
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the last (fewer than 2D) groups
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (g0 + d < G) {
+      consume(g0 + d, d);
+      if (g0 + d + D < G) issue(g0 + d + D, d);
+    }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (g0 + D + d < G) consume(g0 + D + d, d);
 }
 
 template <int NS, int WAVES, bool GATE_UP>
