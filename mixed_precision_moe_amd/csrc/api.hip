@@ -325,7 +325,7 @@ hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, co
   e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
   if (e != hipSuccess) return e;
   st.rec(2);
-  return launch_permute(ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
+  return launch_permute(L.table, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
                         at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
                         at<int32_t>(ws, p.ntiles2), gp.bm2, st.s);
 }

@@ -78,6 +78,10 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t
   return make_uint2(v[0], v[1]);
 }
 
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // fp16 value j (0..3) of four packed in a uint2, as fp32
 __device__ __forceinline__ float half_of(uint2 v, int j) {
   const uint32_t w = j < 2 ? v.x : v.y;

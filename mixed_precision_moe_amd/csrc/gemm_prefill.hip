@@ -39,7 +39,6 @@ constexpr int kPrefillThreads = 256;
 constexpr size_t kPrefillLds = (size_t)2 * 2 * PBM * PLD * sizeof(uint16_t);   // 147456 B
 
 struct PrefillArgs {
-  const DevHandle* table;
   const TileEntry* tiles;
   const int32_t* ntiles;
   int max_tiles;
@@ -345,10 +344,8 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
   te.expert = uniform(te.expert);
   te.row_start = uniform(te.row_start);
   te.rows = uniform(te.rows);
-  DevHandle h = a.table[te.expert];
-  h.tier = uniform(h.tier);
-  h.w13 = uniform_ptr(h.w13);
-  h.w2 = uniform_ptr(h.w2);
+  te.tier = uniform(te.tier);
+  te.w = uniform_ptr(te.w);
   const int tid = threadIdx.x;
   const int n_block = nb * PBN;
 
@@ -362,9 +359,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
     arow[q] = GATE_UP ? a.sorted[pos] / a.top_k : pos;
   }
 
-  const uint8_t* blob = GATE_UP ? h.w13 : h.w2;
+  const uint8_t* blob = te.w;
   lds_u16* lds = (lds_u16*)plds;
-  switch (h.tier) {
+  switch (te.tier) {
     case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP>(a, te, blob, arow, n_block, lds); break;
     case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP>(a, te, blob, arow, n_block, lds); break;
     default: prefill_body<MOE_TIER_BF16, GATE_UP>(a, te, blob, arow, n_block, lds); break;
@@ -396,7 +393,6 @@ hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
                           uint16_t* act16, const float* topk_w, float* rows, hipStream_t s) {
   PrefillArgs a{};
-  a.table = L.table;
   a.tiles = tiles;
   a.ntiles = ntiles;
   a.max_tiles = max_tiles;

@@ -1,4 +1,5 @@
-// grouped_gemm.hip -- grouped expert GEMMs of the MoE layer on gfx950 MFMA.
+// grouped_gemm.hip -- grouped expert GEMMs of the MoE layer for few tokens per
+// expert (decode), on gfx950 MFMA, and the routing-weighted combine.
 //
 // "Every Expert Counts: ExactMoE ..." §3.4: one fused gate/up grouped GEMM and
 // one down grouped GEMM per call over the whole token matrix (no per-expert
@@ -6,10 +7,11 @@
 // weights define the operation (no fp16 expert is materialized); MxMoE
 // (abstract): experts of different precisions run in the same grouped launch.
 //
-// One workgroup computes a BM x BN output tile of one expert.  Its M-tile comes
-// from the device tile table written by the grouping kernel (rows of the
-// expert's segment of the grouped route order); the expert's precision tier and
-// packed weights come from the handle table, so one launch serves all tiers.
+// One workgroup computes an M-tile x (WAVES*NS*16)-column tile of one expert.
+// Its M-tile comes from the device tile table written by the grouping kernel
+// (rows of the expert's segment of the grouped route order, plus the expert's
+// precision tier and packed weights copied from the handle table), so one
+// launch serves all tiers.
 //
 // Numerics.  Weights reach the MFMA as exact integers: an int4 code u = q+8 is
 // turned into the bf16 value 136+q with one and-or (0x4300 | u), an int8 code
@@ -23,7 +25,7 @@
 // Packed layout: see quant_pack.hip.  A 16-byte load per lane of one 1 KB tile
 // gives that lane's B operands for four consecutive 32-wide MFMA k-steps of
 // one 16-column strip (int4), so B goes from HBM to registers with no LDS and
-// no cross-lane shuffles.  A (activations) is staged through LDS per k-group.
+// no cross-lane shuffles.  A (activations) is staged through LDS once.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout used here: lane l holds row
 // (A) / column (B) l%16 and the 8 k-values 8*(l/16) .. +7 of the 32-wide step;
@@ -37,7 +39,6 @@ namespace moe {
 namespace {
 
 struct GemmArgs {
-  const DevHandle* table;
   const TileEntry* tiles;
   const int32_t* ntiles;
   const uint16_t* a_src;     // gate/up: x [T, H]; down: act [T*k, I] in grouped order
@@ -55,7 +56,6 @@ struct GemmArgs {
   float* rows;               // [T*k, H] fp32, grouped order
 };
 
-constexpr int kLdsStride = kGroup + 8;   // bf16 per LDS row (272 B: conflict-free reads)
 
 template <int TIER>
 struct TierTraits;
@@ -113,276 +113,6 @@ __device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>:
   }
 }
 
-// Block: WN waves side by side along N; every wave covers all BM = 16*RT rows
-// and NS 16-column strips.  BN = 16*NS*WN.
-template <int RT, int NS, int WN>
-struct Tile {
-  static constexpr int BM = 16 * RT;
-  static constexpr int BN = 16 * NS * WN;
-  static constexpr int kThreads = 64 * WN;
-  static constexpr int kChunks = BM * (kGroup / 8);          // 16-byte A chunks per group
-  static constexpr int kChunksPerThread = (kChunks + kThreads - 1) / kThreads;
-};
-
-template <int TIER, int RT, int NS, int WN, bool GATE_UP>
-__device__ __forceinline__ void mainloop(const GemmArgs& a, const DevHandle& h, bool gate_up,
-                                         int strip0, const uint16_t* const (&arow)[Tile<RT, NS, WN>::kChunksPerThread],
-                                         const int (&acol)[Tile<RT, NS, WN>::kChunksPerThread],
-                                         const int (&alds)[Tile<RT, NS, WN>::kChunksPerThread],
-                                         const float* const (&rrow)[RT][4], uint16_t* lds,
-                                         f32x4_t (&acc)[RT][NS]) {
-  using TT = Tile<RT, NS, WN>;
-  using TR = TierTraits<TIER>;
-  const Int4Consts c4 = int4_consts();
-  const int lane = threadIdx.x & 63;
-  const int K = a.K, G = K / kGroup;
-  const uint8_t* blob = gate_up ? h.w13 : h.w2;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_payload<TIER>(a.N, K));
-  const int quad = strip0 >> 2;          // NS = 4 strips = one quad of the layout
-
-  float row_scale[NS];
-  if constexpr (TIER == MOE_TIER_INT8) {
-    const uint2 rs4 = buffer_load8(rsrc, 8 * (lane & 15), (uint32_t)a.N * K + 128u * quad);
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, ns);
-  }
-
-  u32x4 b_cur[NS][TR::kLoads], b_nxt[NS][TR::kLoads];
-  u32x4 a_nxt[TT::kChunksPerThread];
-
-  uint2 s_cur = make_uint2(0, 0), s_nxt = make_uint2(0, 0);   // int4 group scales
-  auto load_b = [&](int g, u32x4 (&dst)[NS][TR::kLoads], uint2& sdst) {
-    const uint32_t block = (uint32_t)(quad * G + g) * TR::kBlockBytes;
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-      for (int q = 0; q < TR::kLoads; ++q)
-        dst[ns][q] = buffer_load16<true>(rsrc, 16 * lane + 1024 * q + ns * TR::kTileBytes, block);
-    if constexpr (TIER == MOE_TIER_INT4) sdst = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
-  };
-  auto load_a = [&](int g) {
-#pragma unroll
-    for (int c = 0; c < TT::kChunksPerThread; ++c)
-      a_nxt[c] = arow[c] ? load_u32x4(arow[c] + kGroup * g + acol[c]) : u32x4{0, 0, 0, 0};
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < TT::kChunksPerThread; ++c)
-      if (alds[c] >= 0)
-        *reinterpret_cast<uint4*>(lds + buf * TT::BM * kLdsStride + alds[c]) =
-            make_uint4(a_nxt[c].x, a_nxt[c].y, a_nxt[c].z, a_nxt[c].w);
-  };
-
-  load_b(0, b_cur, s_cur);
-  load_a(0);
-  store_a(0);
-  __syncthreads();
-
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) {
-      load_b(g + 1, b_nxt, s_nxt);
-      load_a(g + 1);
-    }
-    f32x4_t p[RT][NS];
-    if constexpr (TIER == MOE_TIER_BF16) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) p[rt][ns] = acc[rt][ns];
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4_t init;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) init[i] = -TR::kOffset * row_sum<GATE_UP>(rrow[rt][i], g);
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) p[rt][ns] = init;
-      }
-    }
-    const uint16_t* la = lds + buf * TT::BM * kLdsStride;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t af[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        af[rt] = as_bf16x8(load_u32x4(la + (16 * rt + (lane & 15)) * kLdsStride + 32 * s +
-                                      8 * (lane >> 4)));
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        const bf16x8_t bf = b_operand<TIER>(b_cur[ns], s, c4);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) p[rt][ns] = mfma16x16x32(af[rt], bf, p[rt][ns]);
-      }
-    }
-    if constexpr (TIER == MOE_TIER_BF16) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) acc[rt][ns] = p[rt][ns];
-    } else {
-      float sc[NS];
-      if constexpr (TIER == MOE_TIER_INT4) {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) sc[ns] = half_of(s_cur, ns);
-      } else {
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns) sc[ns] = row_scale[ns];
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rt][ns][i] = __builtin_fmaf(sc[ns], p[rt][ns][i], acc[rt][ns][i]);
-    }
-    if (g + 1 < G) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-        for (int q = 0; q < TR::kLoads; ++q) b_cur[ns][q] = b_nxt[ns][q];
-      s_cur = s_nxt;
-    }
-    __syncthreads();
-  }
-}
-
-template <int RT, int NS, int WN, bool GATE_UP>
-__global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
-  using TT = Tile<RT, NS, WN>;
-  static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
-  const int tile_idx = blockIdx.y;
-  if (tile_idx >= uniform(*a.ntiles)) return;
-  TileEntry te = a.tiles[tile_idx];
-  te.expert = uniform(te.expert);
-  te.row_start = uniform(te.row_start);
-  te.rows = uniform(te.rows);
-  DevHandle h = a.table[te.expert];
-  h.tier = uniform(h.tier);
-  h.w13 = uniform_ptr(h.w13);
-  h.w2 = uniform_ptr(h.w2);
-  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n_block = blockIdx.x * TT::BN;
-  const int strip0 = (n_block + wave * 16 * NS) / 16;
-
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * TT::BM * kLdsStride];
-
-  // A staging role of this thread: chunk c -> (row, 16-byte column)
-  const uint16_t* arow[TT::kChunksPerThread];
-  int acol[TT::kChunksPerThread], alds[TT::kChunksPerThread];
-  const int G = a.K / kGroup;
-#pragma unroll
-  for (int c = 0; c < TT::kChunksPerThread; ++c) {
-    const int chunk = threadIdx.x + c * TT::kThreads;
-    const int m = chunk >> 4, col = 8 * (chunk & 15);
-    arow[c] = nullptr;
-    acol[c] = col;
-    alds[c] = -1;
-    if (chunk < TT::kChunks) {
-      alds[c] = m * kLdsStride + col;
-      if (m < te.rows) {
-        const int pos = te.row_start + m;
-        if constexpr (GATE_UP)
-          arow[c] = a.a_src + (size_t)(a.sorted[pos] / a.top_k) * a.K;
-        else
-          arow[c] = a.a_src + (size_t)pos * a.K;
-      }
-    }
-  }
-  // rows of the accumulator this lane holds, and their R rows
-  const float* rrow[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * rt + 4 * (lane >> 4) + i;
-      rrow[rt][i] = nullptr;
-      if (m < te.rows) {
-        const int pos = te.row_start + m;
-        if constexpr (GATE_UP)
-          rrow[rt][i] = a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G;
-        else
-          rrow[rt][i] = a.rsum + (size_t)pos * (a.K / 32);
-      }
-    }
-
-  f32x4_t acc[RT][NS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) acc[rt][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  switch (h.tier) {
-    case MOE_TIER_INT4:
-      mainloop<MOE_TIER_INT4, RT, NS, WN, GATE_UP>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
-      break;
-    case MOE_TIER_INT8:
-      mainloop<MOE_TIER_INT8, RT, NS, WN, GATE_UP>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
-      break;
-    default:
-      mainloop<MOE_TIER_BF16, RT, NS, WN, GATE_UP>(a, h, GATE_UP, strip0, arow, acol, alds, rrow, lds, acc);
-      break;
-  }
-
-  if constexpr (GATE_UP) {
-    // SwiGLU: strips 4q, 4q+1 are gate, 4q+2, 4q+3 the matching up columns.
-    float rs[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs[rt][i] = 0.0f;
-#pragma unroll
-    for (int q = 0; q < NS / 4; ++q) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ns = 4 * q + half;
-        const int icol = 32 * (strip0 / 4 + q) + 16 * half + (lane & 15);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 16 * rt + 4 * (lane >> 4) + i;
-            const float gv = acc[rt][ns][i], uv = acc[rt][ns + 2][i];
-            const uint32_t a16 = f32_to_bf16_rne(silu_f32(gv) * uv);
-            if (m < te.rows) {
-              a.act[(size_t)(te.row_start + m) * a.I + icol] = (uint16_t)a16;
-              rs[rt][i] += bf16_to_f32(a16);
-            }
-          }
-      }
-    }
-    // per-row sums of this wave's 32 activation columns (fixed order: strips,
-    // then a butterfly over the 16 lanes of a row group)
-    const int P = a.I / 32;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = rs[rt][i];
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
-        const int m = 16 * rt + 4 * (lane >> 4) + i;
-        if ((lane & 15) == 0 && m < te.rows)
-          a.r2[(size_t)(te.row_start + m) * P + strip0 / 4] = v;
-      }
-  } else {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * rt + 4 * (lane >> 4) + i;
-        if (m < te.rows) {
-          const int pos = te.row_start + m;
-          const float wgt = a.topk_w[a.sorted[pos]];
-          float* out = a.rows + (size_t)pos * a.N + n_block + wave * 16 * NS + (lane & 15);
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns) out[16 * ns] = wgt * acc[rt][ns][i];
-        }
-      }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Decode kernel: few rows per expert (an M-tile of at most 16 routes), so the
 // cost is streaming the expert's weights from HBM.  A block of WAVES waves
@@ -391,7 +121,7 @@ __global__ __launch_bounds__(64 * WN) void grouped_gemm_kernel(GemmArgs a) {
 // LDS once, while every wave already has its first weight loads in flight;
 // after that single barrier each wave streams its strips over the whole K with
 // the next D k-groups of weights and scales in flight, reading A fragments
-// from LDS (rows beyond the tile's count are zero and never read).  For a
+// from LDS (rows beyond the tile's count feed only rows that are never stored).  For a
 // gate/up matrix NS = 4 covers 32 gate and the matching 32 up columns.
 // ---------------------------------------------------------------------------
 // s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
@@ -412,7 +142,10 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   const int lda = K + 8;                      // LDS row stride (bf16)
   const int rows = te.rows;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_payload<TIER>(a.N, K));
-  const int quad = strip0 >> 2;          // NS = 4 strips = one quad of the layout
+  // The wave's NS strips are strips u0 .. u0+NS-1 of quad `quad` (NS divides 4).
+  const int quad = strip0 >> 2, u0 = strip0 & 3;
+  const uint32_t tile_voff = 16 * lane + u0 * TR::kTileBytes;
+  const uint32_t scale_voff = 8 * (lane & 15) + 2 * u0;   // fp16 scales of row lane%16, strips u0..
 
   u32x4 bb[D][NS][L];
   uint2 sc[D];
@@ -422,8 +155,15 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
       for (int q = 0; q < L; ++q)
-        bb[d][ns][q] = buffer_load16<true>(rsrc, 16 * lane + 1024 * q + ns * TR::kTileBytes, block);
-    if constexpr (TIER == MOE_TIER_INT4) sc[d] = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
+        bb[d][ns][q] = buffer_load16<true>(rsrc, tile_voff + 1024 * q + ns * TR::kTileBytes, block);
+    if constexpr (TIER == MOE_TIER_INT4) {
+      if constexpr (NS == 4)
+        sc[d] = buffer_load8(rsrc, scale_voff, block + 4096u);
+      else if constexpr (NS == 2)
+        sc[d] = make_uint2(buffer_load4(rsrc, scale_voff, block + 4096u), 0u);
+      else
+        sc[d] = make_uint2(buffer_load_u16(rsrc, scale_voff, block + 4096u), 0u);
+    }
   };
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -463,7 +203,7 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   if constexpr (TIER == MOE_TIER_INT8) {
     const uint2 rs4 = buffer_load8(rsrc, 8 * (lane & 15), (uint32_t)a.N * K + 128u * quad);
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, ns);
+    for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, u0 + ns);
   }
   // A fragments: lane l reads LDS row l % 8.  MFMA rows 8..15 (and rows at or
   // beyond the tile's count) then hold copies or stale data; they only feed
@@ -538,6 +278,7 @@ template <int NS, int WAVES, bool GATE_UP>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
+  static_assert(NS == 1 || NS == 2 || NS == 4, "a wave's strips lie in one quad");
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   const int tile_idx = blockIdx.x / blocks_per_tile;
   const int nb = blockIdx.x - tile_idx * blocks_per_tile;
@@ -546,10 +287,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   te.expert = uniform(te.expert);
   te.row_start = uniform(te.row_start);
   te.rows = uniform(te.rows);
-  DevHandle h = a.table[te.expert];
-  h.tier = uniform(h.tier);
-  h.w13 = uniform_ptr(h.w13);
-  h.w2 = uniform_ptr(h.w2);
+  te.tier = uniform(te.tier);
+  te.w = uniform_ptr(te.w);
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int chunk = nb * WAVES + wave;       // this wave's group of NS strips
   const int strip0 = chunk * NS;
@@ -559,8 +298,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   f32x4_t acc[NS];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint8_t* blob = GATE_UP ? h.w13 : h.w2;
-  switch (h.tier) {
+  const uint8_t* blob = te.w;
+  switch (te.tier) {
     case MOE_TIER_INT4:
       decode_mainloop<MOE_TIER_INT4, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
@@ -639,14 +378,6 @@ hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s) {
   return run(std::integral_constant<int, 4>{});   // N is a multiple of 256: chunks % 4 == 0
 }
 
-template <int RT, bool GATE_UP>
-hipError_t launch_gg(const GemmArgs& a, int max_tiles, hipStream_t s) {
-  constexpr int NS = 4, WN = 4;
-  using TT = Tile<RT, NS, WN>;
-  const dim3 grid(a.N / TT::BN, max_tiles);
-  hipLaunchKernelGGL((grouped_gemm_kernel<RT, NS, WN, GATE_UP>), grid, dim3(TT::kThreads), 0, s, a);
-  return hipGetLastError();
-}
 
 // Sum of a token's k weighted rows in ascending expert order, fp32.
 template <bool BF16_OUT>
@@ -691,7 +422,6 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
                          hipStream_t s) {
   (void)T;
   GemmArgs a{};
-  a.table = L.table;
   a.tiles = tiles;
   a.ntiles = ntiles;
   a.a_src = x;
@@ -703,8 +433,8 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.act = act;
   a.r2 = r2;
   a.I = L.I;
-  if (gp.kind == kGemmDecode) return launch_decode<4, true>(a, max_tiles, s);
-  return launch_gg<4, true>(a, max_tiles, s);
+  if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
+  return launch_decode<4, true>(a, max_tiles, s);
 }
 
 hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
@@ -713,7 +443,6 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
                         hipStream_t s) {
   (void)T;
   GemmArgs a{};
-  a.table = L.table;
   a.tiles = tiles;
   a.ntiles = ntiles;
   a.a_src = act;
@@ -724,8 +453,8 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.N = L.H;
   a.topk_w = topk_w;
   a.rows = rows;
-  if (gp.kind == kGemmDecode) return launch_decode<4, false>(a, max_tiles, s);
-  return launch_gg<4, false>(a, max_tiles, s);
+  if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
+  return launch_decode<4, false>(a, max_tiles, s);
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pos, int T, int H, int k, void* y,

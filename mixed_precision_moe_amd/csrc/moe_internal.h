@@ -24,13 +24,19 @@ struct DevHandle {
 static_assert(sizeof(DevHandle) == sizeof(moe_expert_handle), "handle layout");
 
 // One M-tile of a grouped GEMM: rows [row_start, row_start + rows) of the
-// grouped (sorted) route order, all owned by `expert`.
+// grouped (sorted) route order, all owned by `expert`.  The grouping kernel
+// copies the expert's current tier and the packed blob this GEMM reads (w13
+// for the gate/up table, w2 for the down table) out of the handle table, so a
+// GEMM workgroup finds its weights with one load instead of two dependent ones.
 struct TileEntry {
   int32_t expert;
   int32_t row_start;
   int32_t rows;
-  int32_t pad;
+  int32_t tier;
+  const uint8_t* w;
+  int64_t pad;
 };
+static_assert(sizeof(TileEntry) == 32, "tile entry is one 32-byte scalar load");
 
 // Kernel family and M-tile size for one forward, picked on the host from T
 // and the layer: decode (few routes per expert, weight streaming, exact
@@ -74,7 +80,7 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const flo
                                 int T, int H, int E, float* logits, float* r13, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t s);
-hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
                           int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
                           hipStream_t s);

@@ -223,9 +223,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
 // the base position of its routes inside each expert's segment; a wave then
 // walks its tokens in order, placing the token's k routes (distinct experts)
 // in one step.  The result is the stable order by (expert, token).
-// Finally the M-tile tables of both grouped GEMMs are written.
+// Finally the M-tile tables of both grouped GEMMs are written, each entry
+// carrying the expert's tier and packed weights from the handle table.
 __global__ __launch_bounds__(1024) void permute_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
+    const DevHandle* __restrict__ table, const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
     int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
     int32_t* __restrict__ ntiles2, int bm2) {
@@ -278,10 +279,11 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   __syncthreads();
 
   // M-tile tables: expert e with c_e routes gets ceil(c_e / bm) tiles
-  for (int table = 0; table < 2; ++table) {
-    const int bm = table == 0 ? bm13 : bm2;
-    TileEntry* tiles = table == 0 ? tiles13 : tiles2;
-    int32_t* ntiles = table == 0 ? ntiles13 : ntiles2;
+  const DevHandle h = table[min(tid, E - 1)];
+  for (int gemm = 0; gemm < 2; ++gemm) {
+    const int bm = gemm == 0 ? bm13 : bm2;
+    TileEntry* tiles = gemm == 0 ? tiles13 : tiles2;
+    int32_t* ntiles = gemm == 0 ? ntiles13 : ntiles2;
     const int ce = tid < E ? off[tid + 1] - off[tid] : 0;
     const int nt = (ce + bm - 1) / bm;
     int tot = 0;
@@ -291,6 +293,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(
       te2.expert = tid;
       te2.row_start = off[tid] + i * bm;
       te2.rows = min(bm, ce - i * bm);
+      te2.tier = h.tier;
+      te2.w = gemm == 0 ? h.w13 : h.w2;
       te2.pad = 0;
       tiles[first + i] = te2;
     }
@@ -322,7 +326,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
                           int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
                           hipStream_t s) {
@@ -335,7 +339,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, ids, T, k, E, offsets, sorted,
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, ids, T, k, E, offsets, sorted,
                      pos, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2);
   return hipGetLastError();
 }
