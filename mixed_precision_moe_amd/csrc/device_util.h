@@ -158,6 +158,11 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about 1 ulp
+// each; the result is rounded to bf16 afterwards).  Large |g| saturate to the
+// right limits: e^-g -> inf gives g * 0, e^-g -> 0 gives g.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g));
+}
 
 }  // namespace moe

@@ -11,12 +11,17 @@
 // magnitudes in [2^-14, 65504]; larger magnitudes saturate to +-65504).
 //
 // Block: 256 threads (2 x 2 waves), tile 256 rows x 256 columns of one expert,
-// K staged in chunks of 64 through double-buffered LDS.  Per chunk the whole
-// block cooperatively loads the activation rows (gathered through the grouped
-// route order) and the packed weights of its 256 columns, dequantizes the
-// weights (one thread per column and strip row) and writes both as fp16 row
-// panels; each wave then runs 8 x 8 v_mfma_f32_16x16x32_f16 tiles (128 x 128)
-// per 32-wide k-step with accumulators in AGPRs.
+// K staged in chunks of 64 through double-buffered LDS.  Activation rows
+// (gathered through the grouped route order) go from memory straight into LDS
+// with buffer_load ... lds: one instruction fills 8 rows x 128 bytes (whole
+// cache lines), 16-byte slots permuted within a row by an XOR of the row
+// index so that the MFMA operand reads hit 16 distinct bank groups.  The
+// packed weights of the block's 256 columns are loaded into registers,
+// dequantized (one thread per column) and written in fragment-major order (a
+// 1 KB fragment holds one 16 x 32 operand with lane l's 16 bytes at 16*l).
+// Each wave reads the operands of both 32-wide k-steps of a chunk, then runs
+// 2 x 8 x 8 v_mfma_f32_16x16x32_f16 (128 x 128 per wave) with accumulators in
+// AGPRs.
 #include <type_traits>
 
 #include "device_util.h"
@@ -29,14 +34,16 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // LDS pointers with their address space spelled out, so every access is a
 // ds_read / ds_write (a generic pointer would become a flat access).
 typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v4u32 lds_u4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef short f16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 
 constexpr int PBM = 256, PBN = 256, PBK = 64;
-constexpr int PLD = PBK + 8;           // LDS row stride in halves (144 B: conflict-free reads)
 constexpr int kPrefillThreads = 256;
-constexpr size_t kPrefillLds = (size_t)2 * 2 * PBM * PLD * sizeof(uint16_t);   // 147456 B
+constexpr int kFragBytes = 1024;                         // one 16 x 32 fp16 operand
+constexpr int kPanelBytes = 2 * (PBM / 16) * kFragBytes; // A or B of one chunk: 32 fragments
+constexpr size_t kPrefillLds = (size_t)2 * 2 * kPanelBytes;   // 2 buffers x (A + B) = 128 KB
 
 struct PrefillArgs {
   const TileEntry* tiles;
@@ -134,11 +141,15 @@ __device__ __forceinline__ void load_b_chunk(BRaw<TIER>& raw, __amdgpu_buffer_rs
   }
 }
 
-// Dequantize the thread's raw chunk and write its column (64 fp16) to LDS.
-// Within the chunk, k-step ks (0, 1) and chunk c hold k = 32 ks + 8 c + i.
+// Dequantize the thread's raw chunk (column r of strip cb, all 64 k) and write
+// it into the B fragments (cb, ks) of the chunk: the 8 values k = 32 ks + 8 c
+// + 0..7 go to lane slot r + 16 c of fragment 2 cb + ks.  `bcol` points at
+// slot r of fragment 2 cb (fragment 2 cb + 1 follows it after 1 KB).
 template <int TIER>
-__device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale,
-                                              lds_u16* brow) {
+__device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale, lds_u8* bcol) {
+  auto put = [&](int ks, int c, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+    *reinterpret_cast<lds_u4*>(bcol + ks * kFragBytes + 256 * c) = v4u32{x0, x1, x2, x3};
+  };
   if constexpr (TIER == MOE_TIER_INT4) {
     const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)raw.scale);
     const half2_t s2 = {sh, sh};
@@ -147,8 +158,8 @@ __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_s
       uint32_t o0[4], o1[4];
       dequant_int4_word(raw.w[c].x, s2, o0);     // k-step 0 of the chunk
       dequant_int4_word(raw.w[c].y, s2, o1);     // k-step 1
-      *reinterpret_cast<lds_u4*>(brow + 8 * c) = v4u32{o0[0], o0[1], o0[2], o0[3]};
-      *reinterpret_cast<lds_u4*>(brow + 32 + 8 * c) = v4u32{o1[0], o1[1], o1[2], o1[3]};
+      put(0, c, o0[0], o0[1], o0[2], o0[3]);
+      put(1, c, o1[0], o1[1], o1[2], o1[3]);
     }
   } else if constexpr (TIER == MOE_TIER_INT8) {
     const _Float16 sh = (_Float16)row_scale;
@@ -160,18 +171,17 @@ __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_s
       dequant_int8_word(raw.w[c].y, s2, b0, b1);   // k-step 0, elements 4..7
       dequant_int8_word(raw.w[c].z, s2, c0, c1);   // k-step 1, elements 0..3
       dequant_int8_word(raw.w[c].w, s2, d0, d1);   // k-step 1, elements 4..7
-      *reinterpret_cast<lds_u4*>(brow + 8 * c) = v4u32{a0, a1, b0, b1};
-      *reinterpret_cast<lds_u4*>(brow + 32 + 8 * c) = v4u32{c0, c1, d0, d1};
+      put(0, c, a0, a1, b0, b1);
+      put(1, c, c0, c1, d0, d1);
     }
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4 v = raw.w[2 * c + s2];
-        *reinterpret_cast<lds_u4*>(brow + 32 * s2 + 8 * c) =
-            v4u32{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
-                  bf16x2_to_f16x2(v.w)};
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 v = raw.w[2 * c + ks];
+        put(ks, c, bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
+            bf16x2_to_f16x2(v.w));
       }
   }
 }
@@ -183,15 +193,18 @@ __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
                                                 __builtin_bit_cast(f16x8v_t, b), c, 0, 0, 0);
 }
 
+// s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uint8_t* blob,
                                                  const int (&arow)[8], int n_block,
-                                                 lds_u16* lds, f32x4_t (&acc)[8][8]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                 lds_u8* lds, f32x4_t (&acc)[8][8]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K, G = K / kGroup, KC = K / PBK;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<TIER>(a.N, K));
-  // weight staging role: strip (tid >> 4: 0..15 in the block), column r
+  // weight staging role: column r of strip cb = 4 qloc + u of the block
   const int qloc = tid >> 6, u = (tid >> 4) & 3, r = tid & 15;
   const int quad0 = n_block / 64;                       // block-uniform
   constexpr int kBlk = PTier<TIER>::kBlock;
@@ -208,66 +221,84 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   if constexpr (TIER == MOE_TIER_INT8)
     row_scale = (float)__builtin_bit_cast(
         _Float16, buffer_load_u16(rsrc, 2 * (64 * qloc + 4 * r + u), (uint32_t)a.N * K + 128u * quad0));
-  // activation staging role: 8 (row, 16-byte column) chunks per thread
-  const int acol = 8 * (tid & 7);
+  // Activation panel: 16-row blocks of 2 KB; row r of a block holds its 64
+  // chunk values (128 B) with the 8-value slice kb in 16-byte slot kb ^ (r/2).
+  // Staging role: wave w fills tile rows 64w .. 64w+63 with 8 DMAs; lane l of
+  // DMA i loads tile row 64w + 8i + l/8 into slot l%8 (slice (l%8) ^ (r/2)).
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a.a16, a.a16_bytes);
   uint32_t avoff[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) avoff[q] = (uint32_t)arow[q] * K * 2u + 2u * acol;
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 8 * (i & 1) + (lane >> 3);              // row within the 16-row block
+    avoff[i] = (uint32_t)arow[i] * K * 2u + 16u * ((lane & 7) ^ (rr >> 1));
+  }
+  // operand read offsets within a 16-row block, k-steps 0 and 1
+  uint32_t aread[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rr = lane & 15, kb = 4 * ks + (lane >> 4);
+    aread[ks] = 128u * rr + 16u * (kb ^ (rr >> 1));
+  }
 
-  // LDS: A buffers at 0 and PBM*PLD, B buffers at 2*PBM*PLD and 3*PBM*PLD
-  auto As = [&](int buf) { return lds + buf * (PBM * PLD); };
-  auto Bs = [&](int buf) { return lds + (2 + buf) * (PBM * PLD); };
+  // LDS: buffer b holds the A panel at b * 2P and the B panel at b * 2P + P
+  auto As = [&](int buf) { return lds + buf * 2 * kPanelBytes; };
+  auto Bs = [&](int buf) { return lds + buf * 2 * kPanelBytes + kPanelBytes; };
 
   BRaw<TIER> braw;
-  u32x4 araw[8];
-  auto load_chunk = [&](int kc) {
+  auto load_b = [&](int kc) {
     const uint32_t soff = (uint32_t)(quad0 * G + (kc >> 1)) * kBlk;
     load_b_chunk<TIER>(braw, rsrc, bvoff, soff, kc & 1);
     if constexpr (TIER == MOE_TIER_INT4) braw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) araw[q] = buffer_load16<false>(arsrc, avoff[q], 2u * PBK * kc);
   };
-  auto store_chunk = [&](int buf) {
-    store_b_chunk<TIER>(braw, row_scale, Bs(buf) + (16 * (tid >> 4) + r) * PLD);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      *reinterpret_cast<lds_u4*>(As(buf) + ((tid >> 3) + 32 * q) * PLD + acol) =
-          v4u32{araw[q].x, araw[q].y, araw[q].z, araw[q].w};
-  };
-
-  const int fr = lane & 15, fk = 8 * (lane >> 4);
-  f16x8_t fa0[8], fb0[8];
-  auto read_frags = [&](int buf, int ks, f16x8_t (&fa)[8], f16x8_t (&fb)[8]) {
-    const lds_u16* Aw = As(buf) + (128 * wm + fr) * PLD + fk + 32 * ks;
-    const lds_u16* Bw = Bs(buf) + (128 * wn + fr) * PLD + fk + 32 * ks;
+  auto dma_a = [&](int kc, int buf) {
+    lds_u8* dst = As(buf) + 8 * wave * 1024;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      fa[i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + 16 * i * PLD));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
+                                               2u * PBK * kc, 0, 0);
+  };
+  auto store_b = [&](int buf) {
+    store_b_chunk<TIER>(braw, row_scale, Bs(buf) + 2 * (4 * qloc + u) * kFragBytes + 16 * r);
+  };
+
+  f16x8_t fa[2][8], fb[2][8];
+  auto read_frags = [&](int buf, int ks) {
+    const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
+    const lds_u8* Bw = Bs(buf) + (2 * 8 * wn + ks) * kFragBytes + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      fb[j] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Bw + 16 * j * PLD));
+      fb[ks][j] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Bw + 2 * j * kFragBytes));
   };
-  auto mfma_block = [&](const f16x8_t (&fa)[8], const f16x8_t (&fb)[8]) {
+  auto mfma_block = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma_f16(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < 8; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
   };
 
-  load_chunk(0);
-  store_chunk(0);
+  load_b(0);
+  dma_a(0, 0);
+  store_b(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  // chunk kc+1 is loaded from memory while chunk kc is multiplied, then
-  // dequantized into the other LDS buffer
+  // chunk kc+1 streams into the other buffer (activations by DMA, weights
+  // through registers, dequantized after the math) while chunk kc is multiplied
   for (int kc = 0; kc < KC; ++kc) {
     const int buf = kc & 1;
-    if (kc + 1 < KC) load_chunk(kc + 1);
-    read_frags(buf, 0, fa0, fb0);
-    mfma_block(fa0, fb0);
-    read_frags(buf, 1, fa0, fb0);
-    mfma_block(fa0, fb0);
-    if (kc + 1 < KC) store_chunk(buf ^ 1);
+    const bool next = kc + 1 < KC;
+    if (next) {
+      dma_a(kc + 1, buf ^ 1);
+      load_b(kc + 1);
+    }
+    read_frags(buf, 0);
+    read_frags(buf, 1);
+    mfma_block(0);
+    mfma_block(1);
+    if (next) store_b(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 }
@@ -284,7 +315,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_as_f16(float v) {
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEntry& te,
                                              const uint8_t* blob, const int (&arow)[8],
-                                             int n_block, lds_u16* plds) {
+                                             int n_block, lds_u8* plds) {
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   f32x4_t acc[8][8];
@@ -331,7 +362,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t plds[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t plds[];
   // Column blocks of one M-tile are adjacent in launch order, so the blocks
   // sharing an activation tile run together (it is read from HBM about once),
   // and consecutive M-tiles of an expert reuse its weights from the last-level
@@ -349,18 +380,19 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
   const int tid = threadIdx.x;
   const int n_block = nb * PBN;
 
-  // activation rows this thread stages (row (tid >> 3) + 32 q); rows past the
-  // tile's count read the tile's last row (their results are never stored)
+  // activation rows this thread's lane loads: row 64 wave + 8 i + lane / 8;
+  // rows past the tile's count read the tile's last row (their results are
+  // never stored)
   int arow[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int m = min((tid >> 3) + 32 * q, te.rows - 1);
+  for (int j = 0; j < 8; ++j) {
+    const int m = min(64 * (tid >> 6) + 8 * j + ((tid & 63) >> 3), te.rows - 1);
     const int pos = te.row_start + m;
-    arow[q] = GATE_UP ? a.sorted[pos] / a.top_k : pos;
+    arow[j] = GATE_UP ? a.sorted[pos] / a.top_k : pos;
   }
 
   const uint8_t* blob = te.w;
-  lds_u16* lds = (lds_u16*)plds;
+  lds_u8* lds = (lds_u8*)plds;
   switch (te.tier) {
     case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP>(a, te, blob, arow, n_block, lds); break;
     case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP>(a, te, blob, arow, n_block, lds); break;
