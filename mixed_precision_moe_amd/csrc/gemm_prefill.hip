@@ -10,18 +10,19 @@
 // Activations enter as fp16 re-encodings of their bf16 values (exact for
 // magnitudes in [2^-14, 65504]; larger magnitudes saturate to +-65504).
 //
-// Block: 256 threads (2 x 2 waves), tile 256 rows x 256 columns of one expert,
-// K staged in chunks of 64 through double-buffered LDS.  Activation rows
-// (gathered through the grouped route order) go from memory straight into LDS
-// with buffer_load ... lds: one instruction fills 8 rows x 128 bytes (whole
-// cache lines), 16-byte slots permuted within a row by an XOR of the row
-// index so that the MFMA operand reads hit 16 distinct bank groups.  The
-// packed weights of the block's 256 columns are loaded into registers,
-// dequantized (one thread per column) and written in fragment-major order (a
-// 1 KB fragment holds one 16 x 32 operand with lane l's 16 bytes at 16*l).
-// Each wave reads the operands of both 32-wide k-steps of a chunk, then runs
-// 2 x 8 x 8 v_mfma_f32_16x16x32_f16 (128 x 128 per wave) with accumulators in
-// AGPRs.
+// Block: 512 threads (8 waves, two per SIMD so that one wave's MFMAs cover
+// the other's waits), tile 256 rows x 256 columns of one expert; wave (wm, wn)
+// of the 2 x 4 grid owns 128 rows x 64 columns (8 x 4 MFMA tiles, 128
+// accumulators in AGPRs).  K is staged in chunks of 64 through double-buffered
+// LDS.  Activation rows (gathered through the grouped route order) go from
+// memory straight into LDS with buffer_load ... lds: one instruction fills 8
+// rows x 128 bytes (whole cache lines), 16-byte slots permuted within a row by
+// an XOR of the row index so that the MFMA operand reads hit 16 distinct bank
+// groups.  The packed weights of the block's 256 columns are loaded into
+// registers, dequantized (one thread per column and k-step) and written in
+// fragment-major order (a 1 KB fragment holds one 16 x 32 operand with lane
+// l's 16 bytes at 16*l).  Each wave reads the operands of both 32-wide k-steps
+// of a chunk, then runs 2 x 8 x 4 v_mfma_f32_16x16x32_f16.
 #include <type_traits>
 
 #include "device_util.h"
@@ -40,7 +41,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short f16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 
 constexpr int PBM = 256, PBN = 256, PBK = 64;
-constexpr int kPrefillThreads = 256;
+constexpr int kPrefillThreads = 512;
 constexpr int kFragBytes = 1024;                         // one 16 x 32 fp16 operand
 constexpr int kPanelBytes = 2 * (PBM / 16) * kFragBytes; // A or B of one chunk: 32 fragments
 constexpr size_t kPrefillLds = (size_t)2 * 2 * kPanelBytes;   // 2 buffers x (A + B) = 128 KB
@@ -106,83 +107,73 @@ __device__ __forceinline__ uint32_t payload_bytes(int N, int K) {
   else return 2u * N * K;
 }
 
-// Weight staging role of one thread: column r of strip `strip` (16 strips of
-// the block), all 64 k of the chunk.  Raw registers hold what the chunk needs:
-// int4 4 x 8 B (chunk c = 0..3, two k-steps each), int8 4 x 16 B, bf16 8 x 16 B.
+// Weight staging role of one thread: column r of strip cb (16 strips of the
+// block), k-step ks (32 k) of the chunk.  Raw registers: int4 4 words (c =
+// 0..3, 8 codes each) + the group scale, int8 4 x 8 B, bf16 4 x 16 B.
 template <int TIER>
 struct BRaw;
 template <>
-struct BRaw<MOE_TIER_INT4> { uint2 w[4]; uint32_t scale; };
+struct BRaw<MOE_TIER_INT4> { uint32_t w[4]; uint32_t scale; };
 template <>
-struct BRaw<MOE_TIER_INT8> { u32x4 w[4]; };
+struct BRaw<MOE_TIER_INT8> { uint2 w[4]; };
 template <>
-struct BRaw<MOE_TIER_BF16> { u32x4 w[8]; };
+struct BRaw<MOE_TIER_BF16> { u32x4 w[4]; };
 
 // voff: this thread's byte offset inside the block's first quad row of blocks
 // (its quad within the block times G blocks, plus the strip and column
 // position); soff: the block-uniform offset of k-group g of the block's first
-// quad.  Everything thread-dependent is in voff, so the loads need no
-// per-lane scalar values.
+// quad; h: which half of the group the chunk is.  In every tier's packed tile,
+// lane slot 16 c + r holds column r's k = 32 s + 8 c + 0..7 for the group's
+// four 32-wide steps s; the chunk's k-step ks is step s = 2 h + ks.
 template <int TIER>
 __device__ __forceinline__ void load_b_chunk(BRaw<TIER>& raw, __amdgpu_buffer_rsrc_t rsrc,
-                                             uint32_t voff, uint32_t soff, int h) {
+                                             uint32_t voff, uint32_t soff, int h, int ks) {
   if constexpr (TIER == MOE_TIER_INT4) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) raw.w[c] = buffer_load8(rsrc, voff + 256 * c + 8 * h, soff);
+    for (int c = 0; c < 4; ++c) raw.w[c] = buffer_load4(rsrc, voff + 256 * c + 4 * (2 * h + ks), soff);
   } else if constexpr (TIER == MOE_TIER_INT8) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) raw.w[c] = buffer_load16<true>(rsrc, voff + 1024 * h + 256 * c, soff);
+    for (int c = 0; c < 4; ++c) raw.w[c] = buffer_load8(rsrc, voff + 1024 * h + 256 * c + 8 * ks, soff);
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        raw.w[2 * c + s2] = buffer_load16<true>(rsrc, voff + 1024 * (2 * h + s2) + 256 * c, soff);
+      raw.w[c] = buffer_load16<true>(rsrc, voff + 1024 * (2 * h + ks) + 256 * c, soff);
   }
 }
 
-// Dequantize the thread's raw chunk (column r of strip cb, all 64 k) and write
-// it into the B fragments (cb, ks) of the chunk: the 8 values k = 32 ks + 8 c
-// + 0..7 go to lane slot r + 16 c of fragment 2 cb + ks.  `bcol` points at
-// slot r of fragment 2 cb (fragment 2 cb + 1 follows it after 1 KB).
+// Dequantize the thread's raw k-step and write it into B fragment (cb, ks):
+// the 8 values k = 32 ks + 8 c + 0..7 go to lane slot r + 16 c.  `bfrag`
+// points at slot r of that fragment.
 template <int TIER>
-__device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale, lds_u8* bcol) {
-  auto put = [&](int ks, int c, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
-    *reinterpret_cast<lds_u4*>(bcol + ks * kFragBytes + 256 * c) = v4u32{x0, x1, x2, x3};
+__device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale, lds_u8* bfrag) {
+  auto put = [&](int c, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+    *reinterpret_cast<lds_u4*>(bfrag + 256 * c) = v4u32{x0, x1, x2, x3};
   };
   if constexpr (TIER == MOE_TIER_INT4) {
     const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)raw.scale);
     const half2_t s2 = {sh, sh};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint32_t o0[4], o1[4];
-      dequant_int4_word(raw.w[c].x, s2, o0);     // k-step 0 of the chunk
-      dequant_int4_word(raw.w[c].y, s2, o1);     // k-step 1
-      put(0, c, o0[0], o0[1], o0[2], o0[3]);
-      put(1, c, o1[0], o1[1], o1[2], o1[3]);
+      uint32_t o[4];
+      dequant_int4_word(raw.w[c], s2, o);
+      put(c, o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (TIER == MOE_TIER_INT8) {
     const _Float16 sh = (_Float16)row_scale;
     const half2_t s2 = {sh, sh};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      uint32_t a0, a1, b0, b1, c0, c1, d0, d1;
-      dequant_int8_word(raw.w[c].x, s2, a0, a1);   // k-step 0, elements 0..3
-      dequant_int8_word(raw.w[c].y, s2, b0, b1);   // k-step 0, elements 4..7
-      dequant_int8_word(raw.w[c].z, s2, c0, c1);   // k-step 1, elements 0..3
-      dequant_int8_word(raw.w[c].w, s2, d0, d1);   // k-step 1, elements 4..7
-      put(0, c, a0, a1, b0, b1);
-      put(1, c, c0, c1, d0, d1);
+      uint32_t a0, a1, b0, b1;
+      dequant_int8_word(raw.w[c].x, s2, a0, a1);   // elements 0..3
+      dequant_int8_word(raw.w[c].y, s2, b0, b1);   // elements 4..7
+      put(c, a0, a1, b0, b1);
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 v = raw.w[2 * c + ks];
-        put(ks, c, bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
-            bf16x2_to_f16x2(v.w));
-      }
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = raw.w[c];
+      put(c, bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+    }
   }
 }
 
@@ -198,19 +189,19 @@ constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uint8_t* blob,
-                                                 const int (&arow)[8], int n_block,
-                                                 lds_u8* lds, f32x4_t (&acc)[8][8]) {
+                                                 const int (&arow)[4], int n_block,
+                                                 lds_u8* lds, f32x4_t (&acc)[8][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int K = a.K, G = K / kGroup, KC = K / PBK;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<TIER>(a.N, K));
-  // weight staging role: column r of strip cb = 4 qloc + u of the block
-  const int qloc = tid >> 6, u = (tid >> 4) & 3, r = tid & 15;
+  // weight staging role: column r of strip cb = 4 qloc + u, k-step ks
+  const int ks_own = tid >> 8, qloc = (tid >> 6) & 3, u = (tid >> 4) & 3, r = tid & 15;
   const int quad0 = n_block / 64;                       // block-uniform
   constexpr int kBlk = PTier<TIER>::kBlock;
   uint32_t bvoff;
   if constexpr (TIER == MOE_TIER_INT4)
-    bvoff = (uint32_t)qloc * G * kBlk + 1024u * u + 16u * r;   // + 256 c + 8 h; scale: see below
+    bvoff = (uint32_t)qloc * G * kBlk + 1024u * u + 16u * r;
   else if constexpr (TIER == MOE_TIER_INT8)
     bvoff = (uint32_t)qloc * G * kBlk + 2048u * u + 16u * r;
   else
@@ -221,14 +212,14 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   if constexpr (TIER == MOE_TIER_INT8)
     row_scale = (float)__builtin_bit_cast(
         _Float16, buffer_load_u16(rsrc, 2 * (64 * qloc + 4 * r + u), (uint32_t)a.N * K + 128u * quad0));
-  // Activation panel: 16-row blocks of 2 KB; row r of a block holds its 64
-  // chunk values (128 B) with the 8-value slice kb in 16-byte slot kb ^ (r/2).
-  // Staging role: wave w fills tile rows 64w .. 64w+63 with 8 DMAs; lane l of
-  // DMA i loads tile row 64w + 8i + l/8 into slot l%8 (slice (l%8) ^ (r/2)).
+  // Activation panel: 16-row blocks of 2 KB; row rr of a block holds its 64
+  // chunk values (128 B) with the 8-value slice kb in 16-byte slot kb ^ (rr/2).
+  // Staging role: wave w fills tile rows 32w .. 32w+31 with 4 DMAs; lane l of
+  // DMA i loads tile row 32w + 8i + l/8 into slot l%8.
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a.a16, a.a16_bytes);
-  uint32_t avoff[8];
+  uint32_t avoff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int rr = 8 * (i & 1) + (lane >> 3);              // row within the 16-row block
     avoff[i] = (uint32_t)arow[i] * K * 2u + 16u * ((lane & 7) ^ (rr >> 1));
   }
@@ -247,36 +238,36 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   BRaw<TIER> braw;
   auto load_b = [&](int kc) {
     const uint32_t soff = (uint32_t)(quad0 * G + (kc >> 1)) * kBlk;
-    load_b_chunk<TIER>(braw, rsrc, bvoff, soff, kc & 1);
+    load_b_chunk<TIER>(braw, rsrc, bvoff, soff, kc & 1, ks_own);
     if constexpr (TIER == MOE_TIER_INT4) braw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
   };
   auto dma_a = [&](int kc, int buf) {
-    lds_u8* dst = As(buf) + 8 * wave * 1024;
+    lds_u8* dst = As(buf) + 4 * wave * 1024;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
                                                2u * PBK * kc, 0, 0);
   };
   auto store_b = [&](int buf) {
-    store_b_chunk<TIER>(braw, row_scale, Bs(buf) + 2 * (4 * qloc + u) * kFragBytes + 16 * r);
+    store_b_chunk<TIER>(braw, row_scale, Bs(buf) + (2 * (4 * qloc + u) + ks_own) * kFragBytes + 16 * r);
   };
 
-  f16x8_t fa[2][8], fb[2][8];
+  f16x8_t fa[2][8], fb[2][4];
   auto read_frags = [&](int buf, int ks) {
     const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
-    const lds_u8* Bw = Bs(buf) + (2 * 8 * wn + ks) * kFragBytes + 16 * lane;
+    const lds_u8* Bw = Bs(buf) + (2 * 4 * wn + ks) * kFragBytes + 16 * lane;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
       fb[ks][j] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Bw + 2 * j * kFragBytes));
   };
   auto mfma_block = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
   };
 
   load_b(0);
@@ -314,35 +305,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_as_f16(float v) {
 // activations for gate/up; routing weight -> fp32 rows for down).
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEntry& te,
-                                             const uint8_t* blob, const int (&arow)[8],
+                                             const uint8_t* blob, const int (&arow)[4],
                                              int n_block, lds_u8* plds) {
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x4_t acc[8][8];
+  const int wm = wave >> 2, wn = wave & 3;
+  f32x4_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   prefill_mainloop<TIER, GATE_UP>(a, blob, arow, n_block, plds, acc);
-  const int col0 = n_block + 128 * wn;     // first packed column of this wave
+  const int col0 = n_block + 64 * wn;      // first packed column of this wave (one quad)
   if constexpr (GATE_UP) {
-    // tiles 4q+0,1 are gate, 4q+2,3 the matching up columns of quad (col0/64 + q)
+    // strips 0, 1 of the quad are gate, 2, 3 the matching up columns
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int half = 0; half < 2; ++half) {
+      const int icol = 32 * (col0 / 64) + 16 * half + (lane & 15);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int icol = 32 * (col0 / 64 + q) + 16 * half + (lane & 15);
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
-            if (m < te.rows) {
-              const float g = acc[i][4 * q + half][e], up = acc[i][4 * q + half + 2][e];
-              a.act16[(size_t)(te.row_start + m) * a.I + icol] = f32_to_bf16_as_f16(silu_f32(g) * up);
-            }
+        for (int e = 0; e < 4; ++e) {
+          const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
+          if (m < te.rows) {
+            const float g = acc[i][half][e], up = acc[i][half + 2][e];
+            a.act16[(size_t)(te.row_start + m) * a.I + icol] = f32_to_bf16_as_f16(silu_f32(g) * up);
           }
-      }
+        }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -354,7 +343,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
           const float wgt = a.topk_w[a.sorted[pos]];
           float* out = a.rows + (size_t)pos * a.N + col0 + (lane & 15);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) out[16 * j] = wgt * acc[i][j][e];
+          for (int j = 0; j < 4; ++j) out[16 * j] = wgt * acc[i][j][e];
         }
       }
   }
@@ -380,13 +369,13 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
   const int tid = threadIdx.x;
   const int n_block = nb * PBN;
 
-  // activation rows this thread's lane loads: row 64 wave + 8 i + lane / 8;
+  // activation rows this thread's lane loads: row 32 wave + 8 i + lane / 8;
   // rows past the tile's count read the tile's last row (their results are
   // never stored)
-  int arow[8];
+  int arow[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = min(64 * (tid >> 6) + 8 * j + ((tid & 63) >> 3), te.rows - 1);
+  for (int j = 0; j < 4; ++j) {
+    const int m = min(32 * (tid >> 6) + 8 * j + ((tid & 63) >> 3), te.rows - 1);
     const int pos = te.row_start + m;
     arow[j] = GATE_UP ? a.sorted[pos] / a.top_k : pos;
   }
