@@ -184,8 +184,12 @@ __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
                                                 __builtin_bit_cast(f16x8v_t, b), c, 0, 0, 0);
 }
 
-// s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
-constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+// s_waitcnt immediate of gfx9 for vmcnt(n), n < 16, with expcnt and lgkmcnt
+// left unconstrained
+constexpr int wait_vmcnt(int n) { return n | (0x7 << 4) | (0xF << 8); }
+// global loads of one chunk's weights per thread
+template <int TIER>
+constexpr int b_loads() { return TIER == MOE_TIER_INT4 ? 5 : 4; }
 
 template <int TIER, bool GATE_UP>
 __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uint8_t* blob,
@@ -194,6 +198,7 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int K = a.K, G = K / kGroup, KC = K / PBK;
+  constexpr int kWaitVmcntB = wait_vmcnt(b_loads<TIER>());
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<TIER>(a.N, K));
   // weight staging role: column r of strip cb = 4 qloc + u, k-step ks
   const int ks_own = tid >> 8, qloc = (tid >> 6) & 3, u = (tid >> 4) & 3, r = tid & 15;
@@ -235,11 +240,12 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   auto As = [&](int buf) { return lds + buf * 2 * kPanelBytes; };
   auto Bs = [&](int buf) { return lds + buf * 2 * kPanelBytes + kPanelBytes; };
 
-  BRaw<TIER> braw;
-  auto load_b = [&](int kc) {
+  // weights of chunk c travel in register slot c % 2, two chunks ahead
+  BRaw<TIER> braw0, braw1;
+  auto load_b = [&](int kc, BRaw<TIER>& raw) {
     const uint32_t soff = (uint32_t)(quad0 * G + (kc >> 1)) * kBlk;
-    load_b_chunk<TIER>(braw, rsrc, bvoff, soff, kc & 1, ks_own);
-    if constexpr (TIER == MOE_TIER_INT4) braw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
+    load_b_chunk<TIER>(raw, rsrc, bvoff, soff, kc & 1, ks_own);
+    if constexpr (TIER == MOE_TIER_INT4) raw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
   };
   auto dma_a = [&](int kc, int buf) {
     lds_u8* dst = As(buf) + 4 * wave * 1024;
@@ -248,8 +254,8 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
                                                2u * PBK * kc, 0, 0);
   };
-  auto store_b = [&](int buf) {
-    store_b_chunk<TIER>(braw, row_scale, Bs(buf) + (2 * (4 * qloc + u) + ks_own) * kFragBytes + 16 * r);
+  auto store_b = [&](int buf, const BRaw<TIER>& raw) {
+    store_b_chunk<TIER>(raw, row_scale, Bs(buf) + (2 * (4 * qloc + u) + ks_own) * kFragBytes + 16 * r);
   };
 
   f16x8_t fa[2][8], fb[2][4];
@@ -270,27 +276,35 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
   };
 
-  load_b(0);
-  dma_a(0, 0);
-  store_b(0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  // chunk kc+1 streams into the other buffer (activations by DMA, weights
-  // through registers, dequantized after the math) while chunk kc is multiplied
-  for (int kc = 0; kc < KC; ++kc) {
+  // One chunk: its successor's activations stream into the other buffer by
+  // DMA and the weights two chunks ahead into a register slot; the
+  // successor's weights (loaded a chunk earlier, so already in registers) are
+  // dequantized into the other buffer ahead of this chunk's MFMAs, with which
+  // the scheduler can interleave them.  Prefetch indices are clamped at the
+  // end of K (a repeated load of the last chunk, never used), so the body has
+  // no branches and the compiler's load waits stay exact.  KC is even (K is a
+  // multiple of 128): unrolled by two, each register slot keeps its role.
+  auto step = [&](int kc, BRaw<TIER>& next_raw, BRaw<TIER>& ahead_raw) {
     const int buf = kc & 1;
-    const bool next = kc + 1 < KC;
-    if (next) {
-      dma_a(kc + 1, buf ^ 1);
-      load_b(kc + 1);
-    }
+    dma_a(min(kc + 1, KC - 1), buf ^ 1);
+    load_b(min(kc + 2, KC - 1), ahead_raw);
     read_frags(buf, 0);
     read_frags(buf, 1);
+    store_b(buf ^ 1, next_raw);
     mfma_block(0);
     mfma_block(1);
-    if (next) store_b(buf ^ 1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntB);   // the successor's DMA is done; the weights ahead may fly
     __syncthreads();
+  };
+  load_b(0, braw0);
+  dma_a(0, 0);
+  load_b(1, braw1);
+  store_b(0, braw0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcntB);
+  __syncthreads();
+  for (int kc = 0; kc < KC; kc += 2) {
+    step(kc, braw1, braw0);
+    step(kc + 1, braw0, braw1);
   }
 }
 
