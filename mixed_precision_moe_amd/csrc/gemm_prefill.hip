@@ -44,7 +44,9 @@ constexpr int PBM = 256, PBN = 256, PBK = 64;
 constexpr int kPrefillThreads = 512;
 constexpr int kFragBytes = 1024;                         // one 16 x 32 fp16 operand
 constexpr int kPanelBytes = 2 * (PBM / 16) * kFragBytes; // A or B of one chunk: 32 fragments
-constexpr size_t kPrefillLds = (size_t)2 * 2 * kPanelBytes;   // 2 buffers x (A + B) = 128 KB
+// 2 buffers x (activations + staged weights) = 128 KB; the int4 path uses the
+// activation half only
+constexpr size_t kPrefillLds = (size_t)2 * 2 * kPanelBytes;
 
 struct PrefillArgs {
   const TileEntry* tiles;
@@ -107,17 +109,17 @@ __device__ __forceinline__ uint32_t payload_bytes(int N, int K) {
   else return 2u * N * K;
 }
 
-// Weight staging role of one thread: column r of strip cb (16 strips of the
-// block), k-step ks (32 k) of the chunk.  Raw registers: int4 4 words (c =
+// Staged weights (int8 and bf16 tiers): staging role of one thread: column r
+// of strip cb (16 strips of the block), k-step ks (32 k) of the chunk.  Raw registers: int4 4 words (c =
 // 0..3, 8 codes each) + the group scale, int8 4 x 8 B, bf16 4 x 16 B.
 template <int TIER>
-struct BRaw;
+struct BStage;
 template <>
-struct BRaw<MOE_TIER_INT4> { uint32_t w[4]; uint32_t scale; };
+struct BStage<MOE_TIER_INT4> { uint32_t w[4]; uint32_t scale; };
 template <>
-struct BRaw<MOE_TIER_INT8> { uint2 w[4]; };
+struct BStage<MOE_TIER_INT8> { uint2 w[4]; };
 template <>
-struct BRaw<MOE_TIER_BF16> { u32x4 w[4]; };
+struct BStage<MOE_TIER_BF16> { u32x4 w[4]; };
 
 // voff: this thread's byte offset inside the block's first quad row of blocks
 // (its quad within the block times G blocks, plus the strip and column
@@ -126,7 +128,7 @@ struct BRaw<MOE_TIER_BF16> { u32x4 w[4]; };
 // lane slot 16 c + r holds column r's k = 32 s + 8 c + 0..7 for the group's
 // four 32-wide steps s; the chunk's k-step ks is step s = 2 h + ks.
 template <int TIER>
-__device__ __forceinline__ void load_b_chunk(BRaw<TIER>& raw, __amdgpu_buffer_rsrc_t rsrc,
+__device__ __forceinline__ void load_b_chunk(BStage<TIER>& raw, __amdgpu_buffer_rsrc_t rsrc,
                                              uint32_t voff, uint32_t soff, int h, int ks) {
   if constexpr (TIER == MOE_TIER_INT4) {
 #pragma unroll
@@ -145,7 +147,7 @@ __device__ __forceinline__ void load_b_chunk(BRaw<TIER>& raw, __amdgpu_buffer_rs
 // the 8 values k = 32 ks + 8 c + 0..7 go to lane slot r + 16 c.  `bfrag`
 // points at slot r of that fragment.
 template <int TIER>
-__device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_scale, lds_u8* bfrag) {
+__device__ __forceinline__ void store_b_chunk(const BStage<TIER>& raw, float row_scale, lds_u8* bfrag) {
   auto put = [&](int c, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
     *reinterpret_cast<lds_u4*>(bfrag + 256 * c) = v4u32{x0, x1, x2, x3};
   };
@@ -177,6 +179,14 @@ __device__ __forceinline__ void store_b_chunk(const BRaw<TIER>& raw, float row_s
   }
 }
 
+// int4 weights of one wave and chunk, straight from the packed layout into
+// registers.  The wave's 64 columns are one quad (strips j = 0..3).  In the
+// int4 tile, lane slot l holds column l % 16's codes k = 32 s + 8 (l / 16) +
+// 0..7 for the group's four 32-wide steps s (word s), which is exactly lane
+// l's v_mfma 16x16x32 B operand of step s; the chunk's k-steps are s = 2h,
+// 2h+1.  Per lane: 8 bytes per strip plus the 4 strips' group scales.
+struct BDirect { uint2 w[4]; uint2 scale; };
+
 typedef _Float16 f16x8v_t __attribute__((__vector_size__(8 * sizeof(_Float16))));
 
 __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
@@ -184,21 +194,135 @@ __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
                                                 __builtin_bit_cast(f16x8v_t, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f16x8_t pack_f16x8(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  return __builtin_bit_cast(f16x8_t, v4u32{x0, x1, x2, x3});
+}
+
+// Dequantize the chunk's int4 codes into the B operands of both k-steps.
+__device__ __forceinline__ void dequant_b(const BDirect& raw, f16x8_t (&fb)[2][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 sh = (_Float16)half_of(raw.scale, j);
+    const half2_t s2 = {sh, sh};
+    uint32_t o[4];
+    dequant_int4_word(raw.w[j].x, s2, o);
+    fb[0][j] = pack_f16x8(o[0], o[1], o[2], o[3]);
+    dequant_int4_word(raw.w[j].y, s2, o);
+    fb[1][j] = pack_f16x8(o[0], o[1], o[2], o[3]);
+  }
+}
+
 // s_waitcnt immediate of gfx9 for vmcnt(n), n < 16, with expcnt and lgkmcnt
 // left unconstrained
 constexpr int wait_vmcnt(int n) { return n | (0x7 << 4) | (0xF << 8); }
-// global loads of one chunk's weights per thread
-template <int TIER>
-constexpr int b_loads() { return TIER == MOE_TIER_INT4 ? 5 : 4; }
 
+// int4 tier: weights straight from memory into MFMA operands.
+template <bool GATE_UP>
+__device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, const uint8_t* blob,
+                                                        const int (&arow)[4], int n_block,
+                                                        lds_u8* lds, f32x4_t (&acc)[8][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int K = a.K, G = K / kGroup, KC = K / PBK;
+  constexpr int kWaitVmcntB = wait_vmcnt(5);            // one chunk's weight loads per lane
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<MOE_TIER_INT4>(a.N, K));
+  const int quad = n_block / 64 + wn;                   // this wave's quad (wave-uniform)
+  constexpr int kBlk = PTier<MOE_TIER_INT4>::kBlock;
+  // Activation panel: 16-row blocks of 2 KB; row rr of a block holds its 64
+  // chunk values (128 B) with the 8-value slice kb in 16-byte slot kb ^ (rr/2).
+  // Staging role: wave w fills tile rows 32w .. 32w+31 with 4 DMAs; lane l of
+  // DMA i loads tile row 32w + 8i + l/8 into slot l%8.
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a.a16, a.a16_bytes);
+  uint32_t avoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 8 * (i & 1) + (lane >> 3);              // row within the 16-row block
+    avoff[i] = (uint32_t)arow[i] * K * 2u + 16u * ((lane & 7) ^ (rr >> 1));
+  }
+  // operand read offsets within a 16-row block, k-steps 0 and 1
+  uint32_t aread[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int rr = lane & 15, kb = 4 * ks + (lane >> 4);
+    aread[ks] = 128u * rr + 16u * (kb ^ (rr >> 1));
+  }
+  auto As = [&](int buf) { return lds + buf * kPanelBytes; };
+
+  // weights of chunk c travel in register slot c % 2, two chunks ahead
+  BDirect braw0, braw1;
+  auto load_b = [&](int kc, BDirect& raw) {
+    const uint32_t block = (uint32_t)(quad * G + (kc >> 1)) * kBlk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw.w[j] = buffer_load8(rsrc, 16 * lane + 1024 * j, block + 8 * (kc & 1));
+    raw.scale = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
+  };
+  auto dma_a = [&](int kc, int buf) {
+    lds_u8* dst = As(buf) + 4 * wave * 1024;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
+                                               2u * PBK * kc, 0, 0);
+  };
+
+  f16x8_t fa[2][8], fb[2][4];
+  auto read_frags = [&](int buf, int ks) {
+    const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
+  };
+  auto mfma_block = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
+  };
+
+  // One chunk: its successor's activations stream into the other buffer by
+  // DMA; this chunk's weights (loaded two chunks ago) are dequantized into
+  // MFMA operands and their register slot refilled with the weights two
+  // chunks ahead.  Prefetch indices are clamped at the end of K (a repeated
+  // load of the last chunk, never used), so the body has no branches and the
+  // compiler's load waits stay exact.  KC is even (K is a multiple of 128):
+  // unrolled by two, each register slot keeps its role.
+  auto step = [&](int kc, BDirect& raw) {
+    const int buf = kc & 1;
+    dma_a(min(kc + 1, KC - 1), buf ^ 1);
+    dequant_b(raw, fb);
+    load_b(min(kc + 2, KC - 1), raw);
+    read_frags(buf, 0);
+    read_frags(buf, 1);
+    mfma_block(0);
+    mfma_block(1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntB);   // the successor's DMA is done; the weights ahead may fly
+    __syncthreads();
+  };
+  load_b(0, braw0);
+  load_b(1, braw1);
+  dma_a(0, 0);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  __syncthreads();
+  for (int kc = 0; kc < KC; kc += 2) {
+    step(kc, braw0);
+    step(kc + 1, braw1);
+  }
+}
+
+// global loads of one chunk's staged weights per thread
+template <int TIER>
+constexpr int staged_loads() { return TIER == MOE_TIER_INT4 ? 5 : 4; }
+
+// int8 and bf16 tiers: the weights, two to four times the int4 bytes, are
+// staged once per block through LDS (dequantized by one thread per column and
+// k-step) instead of being fetched by both waves that share a column range.
 template <int TIER, bool GATE_UP>
-__device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uint8_t* blob,
+__device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, const uint8_t* blob,
                                                  const int (&arow)[4], int n_block,
                                                  lds_u8* lds, f32x4_t (&acc)[8][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int K = a.K, G = K / kGroup, KC = K / PBK;
-  constexpr int kWaitVmcntB = wait_vmcnt(b_loads<TIER>());
+  constexpr int kWaitVmcntB = wait_vmcnt(staged_loads<TIER>());
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<TIER>(a.N, K));
   // weight staging role: column r of strip cb = 4 qloc + u, k-step ks
   const int ks_own = tid >> 8, qloc = (tid >> 6) & 3, u = (tid >> 4) & 3, r = tid & 15;
@@ -241,8 +365,8 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   auto Bs = [&](int buf) { return lds + buf * 2 * kPanelBytes + kPanelBytes; };
 
   // weights of chunk c travel in register slot c % 2, two chunks ahead
-  BRaw<TIER> braw0, braw1;
-  auto load_b = [&](int kc, BRaw<TIER>& raw) {
+  BStage<TIER> braw0, braw1;
+  auto load_b = [&](int kc, BStage<TIER>& raw) {
     const uint32_t soff = (uint32_t)(quad0 * G + (kc >> 1)) * kBlk;
     load_b_chunk<TIER>(raw, rsrc, bvoff, soff, kc & 1, ks_own);
     if constexpr (TIER == MOE_TIER_INT4) raw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
@@ -254,7 +378,7 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
                                                2u * PBK * kc, 0, 0);
   };
-  auto store_b = [&](int buf, const BRaw<TIER>& raw) {
+  auto store_b = [&](int buf, const BStage<TIER>& raw) {
     store_b_chunk<TIER>(raw, row_scale, Bs(buf) + (2 * (4 * qloc + u) + ks_own) * kFragBytes + 16 * r);
   };
 
@@ -284,7 +408,7 @@ __device__ __forceinline__ void prefill_mainloop(const PrefillArgs& a, const uin
   // end of K (a repeated load of the last chunk, never used), so the body has
   // no branches and the compiler's load waits stay exact.  KC is even (K is a
   // multiple of 128): unrolled by two, each register slot keeps its role.
-  auto step = [&](int kc, BRaw<TIER>& next_raw, BRaw<TIER>& ahead_raw) {
+  auto step = [&](int kc, BStage<TIER>& next_raw, BStage<TIER>& ahead_raw) {
     const int buf = kc & 1;
     dma_a(min(kc + 1, KC - 1), buf ^ 1);
     load_b(min(kc + 2, KC - 1), ahead_raw);
@@ -328,7 +452,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  prefill_mainloop<TIER, GATE_UP>(a, blob, arow, n_block, plds, acc);
+  if constexpr (TIER == MOE_TIER_INT4)
+    prefill_mainloop_direct<GATE_UP>(a, blob, arow, n_block, plds, acc);
+  else
+    prefill_mainloop_staged<TIER, GATE_UP>(a, blob, arow, n_block, plds, acc);
   const int col0 = n_block + 64 * wn;      // first packed column of this wave (one quad)
   if constexpr (GATE_UP) {
     // strips 0, 1 of the quad are gate, 2, 3 the matching up columns
