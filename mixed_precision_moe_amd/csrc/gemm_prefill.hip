@@ -12,17 +12,20 @@
 //
 // Block: 512 threads (8 waves, two per SIMD so that one wave's MFMAs cover
 // the other's waits), tile 256 rows x 256 columns of one expert; wave (wm, wn)
-// of the 2 x 4 grid owns 128 rows x 64 columns (8 x 4 MFMA tiles, 128
-// accumulators in AGPRs).  K is staged in chunks of 64 through double-buffered
-// LDS.  Activation rows (gathered through the grouped route order) go from
-// memory straight into LDS with buffer_load ... lds: one instruction fills 8
-// rows x 128 bytes (whole cache lines), 16-byte slots permuted within a row by
-// an XOR of the row index so that the MFMA operand reads hit 16 distinct bank
-// groups.  The packed weights of the block's 256 columns are loaded into
-// registers, dequantized (one thread per column and k-step) and written in
-// fragment-major order (a 1 KB fragment holds one 16 x 32 operand with lane
-// l's 16 bytes at 16*l).  Each wave reads the operands of both 32-wide k-steps
-// of a chunk, then runs 2 x 8 x 4 v_mfma_f32_16x16x32_f16.
+// of the 2 x 4 grid owns 128 rows x 64 columns (one quad of the packed layout;
+// 8 x 4 MFMA tiles, 128 fp32 accumulators).  K runs in chunks of 64 with the
+// activation panel double-buffered in LDS: rows (gathered through the grouped
+// route order) go from memory straight into LDS with buffer_load ... lds, one
+// instruction filling 8 rows x 128 bytes (whole cache lines), 16-byte slots
+// permuted within a row by an XOR of the row index so that the MFMA operand
+// reads hit 16 distinct bank groups.  Weights: an int4 lane word of the packed
+// tile is exactly that lane's B operand of one 32-wide k-step, so int4 codes
+// go from memory into registers two chunks ahead and are dequantized there;
+// int8 and bf16 weights (two and four times the bytes) are loaded once per
+// block, dequantized by one thread per column and k-step and staged through
+// LDS in fragment-major order (a 1 KB fragment holds one 16 x 32 operand with
+// lane l's 16 bytes at 16*l).  Each chunk: 2 x 8 x 4 v_mfma_f32_16x16x32_f16
+// per wave.
 #include <type_traits>
 
 #include "device_util.h"
