@@ -53,6 +53,8 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
   w.offsets = take(sizeof(int32_t) * (L.E + 1));
   w.sorted = take(sizeof(int32_t) * R);
   w.pos = take(sizeof(int32_t) * R);
+  w.rank = take(sizeof(int32_t) * R);
+  w.chunk_counts = take(sizeof(int32_t) * (size_t)((T + kPermChunk - 1) / kPermChunk) * L.E);
   w.tiles13 = take(sizeof(TileEntry) * (size_t)(w.max_tiles13 > 0 ? w.max_tiles13 : 1));
   w.ntiles13 = take(sizeof(int32_t));
   w.tiles2 = take(sizeof(TileEntry) * (size_t)(w.max_tiles2 > 0 ? w.max_tiles2 : 1));
@@ -327,7 +329,8 @@ hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, co
   st.rec(2);
   return launch_permute(L.table, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
                         at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
-                        at<int32_t>(ws, p.ntiles2), gp.bm2, st.s);
+                        at<int32_t>(ws, p.ntiles2), gp.bm2, at<int32_t>(ws, p.rank),
+                        at<int32_t>(ws, p.chunk_counts), st.s);
 }
 
 }  // namespace

@@ -13,6 +13,8 @@ constexpr int kGroup = 128;        // int4 group size and the k-tile of every la
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kBlobAlign = 256;
+constexpr int kPermSmallT = 1024;  // largest T grouped by the single-workgroup kernel
+constexpr int kPermChunk = 256;    // tokens per block of the multi-block grouping
 
 // Device copy of one expert handle (same field order as moe_expert_handle).
 struct DevHandle {
@@ -51,6 +53,7 @@ struct GemmPlan {
 // Byte offsets of the workspace regions for T tokens.
 struct WsPlan {
   size_t logits, ids, weights, offsets, sorted, pos, tiles13, ntiles13, tiles2, ntiles2;
+  size_t rank, chunk_counts;
   size_t r13, act, r2, rows, x16;
   size_t total;
   int max_tiles13, max_tiles2;
@@ -80,10 +83,13 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const flo
                                 int T, int H, int E, float* logits, float* r13, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t s);
-hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E, int32_t* offsets,
-                          int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
-                          int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
-                          hipStream_t s);
+// Grouping: one workgroup for T <= kPermSmallT, else a rank pass and a
+// scatter pass over blocks of kPermChunk tokens (rank [T*k] and chunk_counts
+// [ceil(T / kPermChunk) * E] are workspace).
+hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E,
+                          int32_t* offsets, int32_t* sorted, int32_t* pos, TileEntry* tiles13,
+                          int32_t* ntiles13, int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                          int32_t* rank, int32_t* chunk_counts, hipStream_t s);
 hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16_t* x,
                          const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
                          int max_tiles, const float* r13, uint16_t* act, float* r2,

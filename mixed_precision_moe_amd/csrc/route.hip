@@ -217,7 +217,38 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
   return base + inc - v;
 }
 
-// Grouping by expert in one workgroup of 1024 threads (16 waves).
+// M-tile tables (1024 threads, expert e = thread e; off[] in LDS): expert e
+// with c_e routes gets ceil(c_e / bm) tiles of each grouped GEMM, each entry
+// carrying the expert's tier and packed weights from the handle table.
+__device__ __forceinline__ void write_tile_tables(const DevHandle* table, const int* off, int E,
+                                                  TileEntry* tiles13, int32_t* ntiles13, int bm13,
+                                                  TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                                                  int* scan) {
+  const int tid = threadIdx.x;
+  const DevHandle h = table[min(tid, E - 1)];
+  for (int gemm = 0; gemm < 2; ++gemm) {
+    const int bm = gemm == 0 ? bm13 : bm2;
+    TileEntry* tiles = gemm == 0 ? tiles13 : tiles2;
+    int32_t* ntiles = gemm == 0 ? ntiles13 : ntiles2;
+    const int ce = tid < E ? off[tid + 1] - off[tid] : 0;
+    const int nt = (ce + bm - 1) / bm;
+    int tot = 0;
+    const int first = block_exclusive_scan(nt, scan, tot);
+    for (int i = 0; i < nt; ++i) {
+      TileEntry te2;
+      te2.expert = tid;
+      te2.row_start = off[tid] + i * bm;
+      te2.rows = min(bm, ce - i * bm);
+      te2.tier = h.tier;
+      te2.w = gemm == 0 ? h.w13 : h.w2;
+      te2.pad = 0;
+      tiles[first + i] = te2;
+    }
+    if (tid == 0) *ntiles = tot;
+  }
+}
+
+// Grouping by expert in one workgroup of 1024 threads (16 waves), for small T.
 // Tokens are split into 16 contiguous chunks, one per wave.  Per-chunk expert
 // histograms (LDS integer atomics, so the counts are exact) give every wave
 // the base position of its routes inside each expert's segment; a wave then
@@ -278,28 +309,86 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
   __syncthreads();
 
-  // M-tile tables: expert e with c_e routes gets ceil(c_e / bm) tiles
-  const DevHandle h = table[min(tid, E - 1)];
-  for (int gemm = 0; gemm < 2; ++gemm) {
-    const int bm = gemm == 0 ? bm13 : bm2;
-    TileEntry* tiles = gemm == 0 ? tiles13 : tiles2;
-    int32_t* ntiles = gemm == 0 ? ntiles13 : ntiles2;
-    const int ce = tid < E ? off[tid + 1] - off[tid] : 0;
-    const int nt = (ce + bm - 1) / bm;
-    int tot = 0;
-    const int first = block_exclusive_scan(nt, scan, tot);
-    for (int i = 0; i < nt; ++i) {
-      TileEntry te2;
-      te2.expert = tid;
-      te2.row_start = off[tid] + i * bm;
-      te2.rows = min(bm, ce - i * bm);
-      te2.tier = h.tier;
-      te2.w = gemm == 0 ? h.w13 : h.w2;
-      te2.pad = 0;
-      tiles[first + i] = te2;
+  write_tile_tables(table, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+}
+
+// Rank pass of the multi-block grouping (large T).  Block c owns the 256
+// tokens [256c, 256c + 256); each of its 4 waves walks 64 of them in order and
+// numbers the routes of every expert within the wave (a token's k routes go
+// to distinct experts, so one step places all of them); the waves' counts
+// then give every route its stable rank among the block's routes of its
+// expert.  Writes rank[r] and the block's per-expert counts.
+__global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __restrict__ ids, int T,
+                                                           int k, int E, int32_t* __restrict__ rank,
+                                                           int32_t* __restrict__ chunk_counts) {
+  __shared__ int cnt[4][kMaxExperts];
+  __shared__ int rk[kPermChunk * kMaxTopK];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kPermChunk;
+  for (int e = tid; e < 4 * kMaxExperts; e += 256) (&cnt[0][0])[e] = 0;
+  __syncthreads();
+  const int tb = min(T, t0 + 64 * wave), te = min(T, tb + 64);
+  for (int t = tb; t < te; ++t) {
+    if (lane < k) {
+      const int e = min(max(ids[t * k + lane], 0), E - 1);
+      rk[(t - t0) * k + lane] = cnt[wave][e];
+      cnt[wave][e] += 1;
     }
-    if (tid == 0) *ntiles = tot;
+    __builtin_amdgcn_wave_barrier();
   }
+  __syncthreads();
+  for (int i = lane; i < (te - tb) * k; i += 64) {
+    const int r = tb * k + i;
+    const int e = min(max(ids[r], 0), E - 1);
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += cnt[w][e];
+    rank[r] = rk[r - t0 * k] + before;
+  }
+  for (int e = tid; e < E; e += 256)
+    chunk_counts[(size_t)blockIdx.x * E + e] = cnt[0][e] + cnt[1][e] + cnt[2][e] + cnt[3][e];
+}
+
+// Scatter pass of the multi-block grouping.  Block c sums the per-block
+// counts into its bases (routes of each expert in blocks before c) and the
+// totals, scans the totals into the expert offsets, and places its routes at
+// offset + base + rank: the stable order by (expert, token).  Block 0 also
+// writes the offsets and the M-tile tables.
+__global__ __launch_bounds__(1024) void permute_scatter_kernel(
+    const DevHandle* __restrict__ table, const int32_t* __restrict__ ids, int T, int k, int E,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ chunk_counts, int nchunks,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
+    TileEntry* __restrict__ tiles13, int32_t* __restrict__ ntiles13, int bm13,
+    TileEntry* __restrict__ tiles2, int32_t* __restrict__ ntiles2, int bm2) {
+  __shared__ int base[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int scan[16];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  int total = 0;
+  if (tid < E) {
+    int b = 0, tot = 0;
+    for (int i = 0; i < nchunks; ++i) {
+      const int v = chunk_counts[(size_t)i * E + tid];
+      b += i < c ? v : 0;
+      tot += v;
+    }
+    base[tid] = b;
+    total = tot;
+  }
+  int all = 0;
+  const int excl = block_exclusive_scan(total, scan, all);
+  if (tid < E) off[tid] = excl;
+  if (tid == 0) off[E] = all;
+  __syncthreads();
+  const int r0 = c * kPermChunk * k, r1 = min(T, (c + 1) * kPermChunk) * k;
+  for (int r = r0 + tid; r < r1; r += 1024) {
+    const int e = min(max(ids[r], 0), E - 1);
+    const int p = off[e] + base[e] + rank[r];
+    sorted[p] = r;
+    pos[r] = p;
+  }
+  if (c != 0) return;
+  for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
+  write_tile_tables(table, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
 }
 
 }  // namespace
@@ -326,10 +415,21 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E, int32_t* offsets,
-                          int32_t* sorted, int32_t* pos, TileEntry* tiles13, int32_t* ntiles13,
-                          int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
-                          hipStream_t s) {
+hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E,
+                          int32_t* offsets, int32_t* sorted, int32_t* pos, TileEntry* tiles13,
+                          int32_t* ntiles13, int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                          int32_t* rank, int32_t* chunk_counts, hipStream_t s) {
+  if (T > kPermSmallT) {
+    const int nchunks = (T + kPermChunk - 1) / kPermChunk;
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nchunks), dim3(256), 0, s, ids, T, k, E, rank,
+                       chunk_counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(1024), 0, s, table, ids, T, k, E,
+                       rank, chunk_counts, nchunks, offsets, sorted, pos, tiles13, ntiles13, bm13,
+                       tiles2, ntiles2, bm2);
+    return hipGetLastError();
+  }
   const size_t lds = sizeof(int) * (16 * (size_t)E + E + 1 + 1024);
   static bool attr_set = false;   // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB)
   if (!attr_set) {

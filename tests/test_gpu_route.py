@@ -32,7 +32,10 @@ def _check_route(st: Setup, layer=None):
 
 
 @pytest.mark.parametrize("cid,T", [(1, 64), (2, 32), (3, 512), (4, 1), (4, 32), (4, 256),
-                                   (4, 4096), (5, 8192), (1, 1), (1, 37), (2, 5)])
+                                   (4, 4096), (5, 8192), (1, 1), (1, 37), (2, 5),
+                                   # multi-block grouping (T > 1024): ragged last block,
+                                   # a one-token last block
+                                   (4, 1300), (4, 1025), (4, 2000)])
 def test_route_bitexact(cid, T):
     _check_route(Setup(cid, T=T))
 
