@@ -20,8 +20,8 @@ namespace {
 
 // Block: 8 half-waves (256 threads) arranged 2 (token groups) x 4 (expert
 // groups).  Each half-wave owns TT tokens x TE experts; block tile is
-// (2*TT) tokens x (4*TE) experts.
-template <int TT, int TE>
+// (2*TT) tokens x (4*TE) experts.  The slab loop takes SG slabs per step.
+template <int TT, int TE, int SG>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wr,
                                                             const float* __restrict__ bias,
@@ -48,40 +48,50 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   // activations of group g (used by the GEMMs to remove their weight offset).
   const bool do_r13 = r13 != nullptr && blockIdx.y == 0 && (hw & 3) == 0;
   const int G = H / kGroup;
-  for (int base = 0; base < H; base += 256) {
-    u32x4 xv[TT], wv[TE];
+  // SG slabs per step, all their loads issued before the step's FMAs
+  for (int base0 = 0; base0 < H; base0 += 256 * SG) {
+    u32x4 xv[SG][TT], wv[SG][TE];
 #pragma unroll
-    for (int a = 0; a < TT; ++a) xv[a] = load_u32x4(xp[a] + base);
+    for (int sg = 0; sg < SG; ++sg) {
+      const int base = base0 + 256 * sg;
 #pragma unroll
-    for (int b = 0; b < TE; ++b) wv[b] = load_u32x4(wp[b] + base);
+      for (int a = 0; a < TT; ++a) xv[sg][a] = base < H ? load_u32x4(xp[a] + base) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float xf[TT], wf[TE];
-#pragma unroll
-      for (int a = 0; a < TT; ++a) {
-        const uint32_t d = (&xv[a].x)[r >> 1];
-        xf[a] = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
-      }
-#pragma unroll
-      for (int b = 0; b < TE; ++b) {
-        const uint32_t d = (&wv[b].x)[r >> 1];
-        wf[b] = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
-      }
-#pragma unroll
-      for (int a = 0; a < TT; ++a)
-#pragma unroll
-        for (int b = 0; b < TE; ++b) acc[a][b] = __builtin_fmaf(xf[a], wf[b], acc[a][b]);
+      for (int b = 0; b < TE; ++b) wv[sg][b] = base < H ? load_u32x4(wp[b] + base) : u32x4{0, 0, 0, 0};
     }
-    if (do_r13) {
 #pragma unroll
-      for (int a = 0; a < TT; ++a) {
-        const u32x4 q = xv[a];
-        float v = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
-                  (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
+    for (int sg = 0; sg < SG; ++sg) {
+      const int base = base0 + 256 * sg;
+      if (base >= H) break;
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
-        const int t = t0 + a;
-        if ((j & 15) == 0 && t < T) r13[(size_t)t * G + base / kGroup + (j >> 4)] = v;
+      for (int r = 0; r < 8; ++r) {
+        float xf[TT], wf[TE];
+#pragma unroll
+        for (int a = 0; a < TT; ++a) {
+          const uint32_t d = (&xv[sg][a].x)[r >> 1];
+          xf[a] = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
+        }
+#pragma unroll
+        for (int b = 0; b < TE; ++b) {
+          const uint32_t d = (&wv[sg][b].x)[r >> 1];
+          wf[b] = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
+        }
+#pragma unroll
+        for (int a = 0; a < TT; ++a)
+#pragma unroll
+          for (int b = 0; b < TE; ++b) acc[a][b] = __builtin_fmaf(xf[a], wf[b], acc[a][b]);
+      }
+      if (do_r13) {
+#pragma unroll
+        for (int a = 0; a < TT; ++a) {
+          const u32x4 q = xv[sg][a];
+          float v = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
+                    (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
+#pragma unroll
+          for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+          const int t = t0 + a;
+          if ((j & 15) == 0 && t < T) r13[(size_t)t * G + base / kGroup + (j >> 4)] = v;
+        }
       }
     }
   }
@@ -125,6 +135,9 @@ extern "C" __device__ int __ockl_wfred_min_i32(int);
 // lanes hold that maximum, a wave min of their expert ids.
 constexpr int kMaxPerLane = kMaxExperts / 64;
 
+// PER (a power of two, PER * 64 >= E) is the compile-time bound of the
+// lane-local loops, so small E does not pay for the largest.
+template <int PER>
 __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                   int k, int32_t* __restrict__ ids,
                                                   float* __restrict__ weights) {
@@ -132,10 +145,10 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logi
   const int t = blockIdx.x;
   if (t >= T) return;
   const float* z = logits + (size_t)t * E;
-  float v[kMaxPerLane];
+  float v[PER];
   const int per = (E + 63) / 64;
 #pragma unroll
-  for (int m = 0; m < kMaxPerLane; ++m) {
+  for (int m = 0; m < PER; ++m) {
     const int e = lane + 64 * m;
     v[m] = (m < per && e < E) ? z[e] : -INFINITY;
   }
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logi
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int m = 0; m < kMaxPerLane; ++m) {
+    for (int m = 0; m < PER; ++m) {
       const int e = lane + 64 * m;
       if (m < per && e < E && !((taken >> m) & 1u) && better(v[m], e, bv, be)) {
         bv = v[m];
@@ -395,15 +408,15 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
 
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
                                 int H, int E, float* logits, float* r13, hipStream_t s) {
-  if (T <= 64) {
-    constexpr int TT = 1, TE = 4;
+  if (T <= 64) {   // few tokens: many small blocks, 8 slabs of loads in flight per step
+    constexpr int TT = 1, TE = 2;
     const dim3 grid((T + 2 * TT - 1) / (2 * TT), (E + 4 * TE - 1) / (4 * TE));
-    hipLaunchKernelGGL((router_logits_kernel<TT, TE>), grid, dim3(256), 0, s, x, wr, bias, T, H,
+    hipLaunchKernelGGL((router_logits_kernel<TT, TE, 8>), grid, dim3(256), 0, s, x, wr, bias, T, H,
                        E, logits, r13);
   } else {
     constexpr int TT = 4, TE = 4;
     const dim3 grid((T + 2 * TT - 1) / (2 * TT), (E + 4 * TE - 1) / (4 * TE));
-    hipLaunchKernelGGL((router_logits_kernel<TT, TE>), grid, dim3(256), 0, s, x, wr, bias, T, H,
+    hipLaunchKernelGGL((router_logits_kernel<TT, TE, 1>), grid, dim3(256), 0, s, x, wr, bias, T, H,
                        E, logits, r13);
   }
   return hipGetLastError();
@@ -411,7 +424,17 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const flo
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
+  const int per = (E + 63) / 64;
+  if (per <= 1)
+    hipLaunchKernelGGL(topk_kernel<1>, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
+  else if (per <= 2)
+    hipLaunchKernelGGL(topk_kernel<2>, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
+  else if (per <= 4)
+    hipLaunchKernelGGL(topk_kernel<4>, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
+  else if (per <= 8)
+    hipLaunchKernelGGL(topk_kernel<8>, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
+  else
+    hipLaunchKernelGGL(topk_kernel<kMaxPerLane>, dim3(T), dim3(64), 0, s, logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
