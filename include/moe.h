@@ -141,7 +141,28 @@ int moe_layer_create(const moe_layer_desc* desc, const moe_expert_handle* table,
 int moe_layer_set_experts(moe_layer_t layer, int32_t first, int32_t count,
                           const moe_expert_handle* handles, void* stream);
 
-/* Free the layer's device table.  The caller must have synchronized every
+/* Wave execution (ExactMoE §3.4, grouped complete-expert execution; Fig. 1):
+ * when the active experts do not all fit in the resident cache of C slots,
+ * the layer runs in waves, each over the complete token matrix with an
+ * explicit map from global expert ids to resident slots in which every other
+ * expert maps to an inactive sentinel, and the wave outputs are accumulated.
+ *
+ * moe_layer_set_slots: put handles into resident slots [first, first+count)
+ * (slot indices 0 .. n_experts-1; handles as for moe_layer_create, validated on
+ * the host, stream-ordered like moe_layer_set_experts; the host array may be
+ * reused on return).
+ *
+ * moe_layer_set_slot_map: install the global-expert-to-slot map.
+ *   expert_to_slot  host int32 [n_experts]: slot of expert e, or -1 (the
+ *                   inactive sentinel).  Every slot it names must have been
+ *                   given a handle by moe_layer_set_slots (MOE_EINVAL).
+ * Stream-ordered; the host array may be reused on return.  A new layer maps
+ * every expert to the sentinel. */
+int moe_layer_set_slots(moe_layer_t layer, int32_t first, int32_t count,
+                        const moe_expert_handle* handles, void* stream);
+int moe_layer_set_slot_map(moe_layer_t layer, const int32_t* expert_to_slot, void* stream);
+
+/* Free the layer's device state.  The caller must have synchronized every
  * stream that has work using the layer. */
 int moe_layer_destroy(moe_layer_t layer);
 
@@ -178,6 +199,18 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
 int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
                       const float* bias, int32_t T, void* y, int y_dtype, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* One wave: as moe_layer_forward, with the router and top-k over all experts
+ * unchanged (weights not renormalized within a wave), but only the experts the
+ * current slot map sends to a slot contribute, each computed from its slot's
+ * handle; every other route contributes nothing.  accumulate = 0: y = the
+ * wave's output; accumulate = 1: y += it (y_dtype must be MOE_DTYPE_F32).
+ * Over waves whose slot maps partition the experts, the accumulated y is the
+ * layer output up to fp32 rounding of the sum order.  Same pointer,
+ * workspace and stream rules as moe_layer_forward. */
+int moe_layer_forward_wave(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
+                           const float* bias, int32_t T, void* y, int y_dtype, int accumulate,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Optional timing hook: when events (hipEvent_t passed as void*) are set, each
  * forward records events[i] before stage i and events[n-1] after the last

@@ -22,8 +22,9 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_packed_size", "moe_quantize_pack", "moe_layer_create", "moe_layer_set_experts",
-    "moe_layer_destroy", "moe_workspace_size", "moe_route", "moe_layer_forward",
-    "moe_layer_set_stage_events", "moe_strerror", "moe_last_error", "moe_abi_version",
+    "moe_layer_set_slots", "moe_layer_set_slot_map", "moe_layer_destroy", "moe_workspace_size",
+    "moe_route", "moe_layer_forward", "moe_layer_forward_wave", "moe_layer_set_stage_events",
+    "moe_strerror", "moe_last_error", "moe_abi_version",
 )
 
 
@@ -62,10 +63,14 @@ def load() -> ctypes.CDLL:
         "moe_layer_create": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertHandle),
                                             vp, ctypes.POINTER(vp)]),
         "moe_layer_set_experts": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(ExpertHandle), vp]),
+        "moe_layer_set_slots": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(ExpertHandle), vp]),
+        "moe_layer_set_slot_map": (ctypes.c_int, [vp, ctypes.POINTER(i32), vp]),
         "moe_layer_destroy": (ctypes.c_int, [vp]),
         "moe_workspace_size": (sz, [vp, i32]),
         "moe_route": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moe_layer_forward": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, ctypes.c_int, vp, sz, vp]),
+        "moe_layer_forward_wave": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, ctypes.c_int, ctypes.c_int,
+                                                  vp, sz, vp]),
         "moe_layer_set_stage_events": (ctypes.c_int, [vp, ctypes.POINTER(vp), i32]),
         "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),

@@ -184,6 +184,44 @@ class Layer:
             return keep
         return run
 
+    def set_slots(self, first: int, handles, stream=None) -> None:
+        """Resident slots [first, first+len) for wave execution; handles as for
+        the constructor: (tier, w13 blob, w2 blob)."""
+        arr = self._handle_array(handles)
+        check(self._lib.moe_layer_set_slots(self._h, first, len(handles), arr, _stream(stream)),
+              "moe_layer_set_slots")
+        self._keep_slots = getattr(self, "_keep_slots", {})
+        for i, h in enumerate(handles):
+            self._keep_slots[first + i] = h
+
+    def set_slot_map(self, expert_to_slot: Sequence[int], stream=None) -> None:
+        """Global expert -> resident slot map of the next waves (-1 = inactive)."""
+        if len(expert_to_slot) != self.n_experts:
+            raise ValueError(f"slot map needs {self.n_experts} entries")
+        arr = (ctypes.c_int32 * self.n_experts)(*[int(v) for v in expert_to_slot])
+        check(self._lib.moe_layer_set_slot_map(self._h, arr, _stream(stream)), "moe_layer_set_slot_map")
+
+    def forward_wave(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                     y: Optional[torch.Tensor] = None, accumulate: bool = False,
+                     out_dtype: torch.dtype = torch.float32,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """One wave over the experts the current slot map sends to slots
+        (y = or y += the wave's output; accumulating needs an fp32 y)."""
+        _require_cuda(x, "x", _BF16)
+        _require_cuda(wr, "wr", _BF16)
+        if bias is not None:
+            _require_cuda(bias, "bias", (torch.float32,))
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.hidden), dtype=out_dtype, device=x.device)
+        _require_cuda(y, "y", (torch.float32, torch.bfloat16))
+        yd = DTYPE_F32 if y.dtype == torch.float32 else DTYPE_BF16
+        ws = self.workspace(T, x.device) if workspace is None else workspace
+        check(self._lib.moe_layer_forward_wave(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), T,
+                                               y.data_ptr(), yd, int(bool(accumulate)), ws.data_ptr(),
+                                               ws.numel(), _stream(stream)), "moe_layer_forward_wave")
+        return y
+
     def set_stage_events(self, events: Optional[Sequence["torch.cuda.Event"]]) -> None:
         """Per-stage timing events (7 torch.cuda.Event with timing), or None."""
         if not events:

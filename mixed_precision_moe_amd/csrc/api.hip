@@ -87,6 +87,16 @@ __global__ void set_handles_kernel(DevHandle* table, int first, int count, Handl
   }
 }
 
+constexpr int kMapPerLaunch = 256;
+struct MapBatch {
+  int32_t v[kMapPerLaunch];
+};
+
+__global__ void set_map_kernel(int32_t* map, int first, int count, MapBatch b) {
+  const int i = threadIdx.x;
+  if (i < count) map[first + i] = b.v[i];
+}
+
 int validate_handles(const moe_expert_handle* h, int count) {
   for (int i = 0; i < count; ++i) {
     if (h[i].tier < MOE_TIER_BF16 || h[i].tier > MOE_TIER_INT4)
@@ -100,6 +110,18 @@ int validate_handles(const moe_expert_handle* h, int count) {
 }
 
 }  // namespace
+
+hipError_t launch_set_slot_map(int32_t* map, const int32_t* host_map, int E, hipStream_t s) {
+  for (int done = 0; done < E; done += kMapPerLaunch) {
+    const int n = E - done < kMapPerLaunch ? E - done : kMapPerLaunch;
+    MapBatch b;
+    for (int i = 0; i < kMapPerLaunch; ++i) b.v[i] = i < n ? (host_map ? host_map[done + i] : -1) : -1;
+    hipLaunchKernelGGL(set_map_kernel, dim3(1), dim3(kMapPerLaunch), 0, s, map, done, n, b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_set_handles(DevHandle* table, int first, int count,
                               const moe_expert_handle* h, hipStream_t s) {
@@ -221,13 +243,25 @@ int moe_layer_create(const moe_layer_desc* d, const moe_expert_handle* table, vo
   L->E = d->n_experts;
   L->k = d->top_k;
   L->n_stage_events = 0;
+  L->table = nullptr;
+  L->slots = nullptr;
+  L->slot_map = nullptr;
+  L->slot_set = new (std::nothrow) uint8_t[L->E]();
+  if (!L->slot_set) {
+    delete L;
+    return set_error(MOE_EINVAL, "out of host memory");
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   rc = check_hip(hipMalloc(&L->table, sizeof(DevHandle) * L->E), "hipMalloc(table)");
-  if (!rc)
-    rc = check_hip(launch_set_handles(L->table, 0, L->E, table,
-                                      reinterpret_cast<hipStream_t>(stream)),
-                   "set_handles launch");
+  if (!rc) rc = check_hip(hipMalloc(&L->slots, sizeof(DevHandle) * L->E), "hipMalloc(slots)");
+  if (!rc) rc = check_hip(hipMalloc(&L->slot_map, sizeof(int32_t) * L->E), "hipMalloc(slot_map)");
+  if (!rc) rc = check_hip(launch_set_handles(L->table, 0, L->E, table, s), "set_handles launch");
+  if (!rc) rc = check_hip(launch_set_slot_map(L->slot_map, nullptr, L->E, s), "set_slot_map launch");
   if (rc) {
     if (L->table) (void)hipFree(L->table);
+    if (L->slots) (void)hipFree(L->slots);
+    if (L->slot_map) (void)hipFree(L->slot_map);
+    delete[] L->slot_set;
     delete L;
     return rc;
   }
@@ -249,13 +283,49 @@ int moe_layer_set_experts(moe_layer_t layer, int32_t first, int32_t count,
                    "set_handles launch");
 }
 
+int moe_layer_set_slots(moe_layer_t layer, int32_t first, int32_t count,
+                        const moe_expert_handle* handles, void* stream) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L || (!handles && count > 0)) return set_error(MOE_EINVAL, "null pointer");
+  if (first < 0 || count < 0 || first + count > L->E)
+    return set_error(MOE_ESHAPE, "slot range [%d, %d) outside [0, %d)", first, first + count, L->E);
+  int rc = validate_handles(handles, count);
+  if (rc) return rc;
+  rc = check_hip(launch_set_handles(L->slots, first, count, handles,
+                                    reinterpret_cast<hipStream_t>(stream)),
+                 "set_slots launch");
+  if (!rc)
+    for (int i = 0; i < count; ++i) L->slot_set[first + i] = 1;
+  return rc;
+}
+
+int moe_layer_set_slot_map(moe_layer_t layer, const int32_t* expert_to_slot, void* stream) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L || !expert_to_slot) return set_error(MOE_EINVAL, "null pointer");
+  for (int e = 0; e < L->E; ++e) {
+    const int v = expert_to_slot[e];
+    if (v == -1) continue;
+    if (v < 0 || v >= L->E)
+      return set_error(MOE_EINVAL, "expert %d: slot %d outside [-1, %d)", e, v, L->E);
+    if (!L->slot_set[v]) return set_error(MOE_EINVAL, "expert %d: slot %d holds no handle", e, v);
+  }
+  return check_hip(launch_set_slot_map(L->slot_map, expert_to_slot, L->E,
+                                       reinterpret_cast<hipStream_t>(stream)),
+                   "set_slot_map launch");
+}
+
 int moe_layer_destroy(moe_layer_t layer) {
   g_err[0] = 0;
   Layer* L = reinterpret_cast<Layer*>(layer);
   if (!L) return set_error(MOE_EINVAL, "null layer");
-  const int rc = check_hip(hipFree(L->table), "hipFree(table)");
+  int rc = check_hip(hipFree(L->table), "hipFree(table)");
+  const int rc2 = check_hip(hipFree(L->slots), "hipFree(slots)");
+  const int rc3 = check_hip(hipFree(L->slot_map), "hipFree(slot_map)");
+  delete[] L->slot_set;
   delete L;
-  return rc;
+  return rc ? rc : rc2 ? rc2 : rc3;
 }
 
 size_t moe_workspace_size(moe_layer_t layer, int32_t T) {
@@ -316,7 +386,7 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
 }
 
-hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, const uint16_t* x,
+hipError_t enqueue_route(const Layer& L, WaveMap wave, const WsPlan& p, const GemmPlan& gp, const uint16_t* x,
                          const uint16_t* wr, const float* bias, int T, float* logits,
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos,
                          float* r13, void* ws, const Stages& st) {
@@ -327,7 +397,7 @@ hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, co
   e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
   if (e != hipSuccess) return e;
   st.rec(2);
-  return launch_permute(L.table, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
+  return launch_permute(L.table, wave, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
                         at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
                         at<int32_t>(ws, p.ntiles2), gp.bm2, at<int32_t>(ws, p.rank),
                         at<int32_t>(ws, p.chunk_counts), st.s);
@@ -335,47 +405,25 @@ hipError_t enqueue_route(const Layer& L, const WsPlan& p, const GemmPlan& gp, co
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const float* bias,
-              int32_t T, int32_t* topk_ids, float* topk_w, float* logits, int32_t* expert_offsets,
-              int32_t* sorted_routes, int32_t* route_pos, void* ws, size_t ws_bytes,
-              void* stream) {
-  g_err[0] = 0;
-  const Layer* L = reinterpret_cast<const Layer*>(layer);
-  WsPlan p;
-  GemmPlan gp;
-  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
-  if (rc) return rc;
-  if (!expert_offsets || (T > 0 && (!topk_ids || !topk_w || !sorted_routes || !route_pos)))
-    return set_error(MOE_EINVAL, "null output pointer");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (T == 0)
-    return check_hip(hipMemsetAsync(expert_offsets, 0, sizeof(int32_t) * (L->E + 1), s),
-                     "hipMemsetAsync(offsets)");
-  const Stages st{L, s, false};
-  const hipError_t e = enqueue_route(*L, p, gp, x, wr, bias, T,
-                                     logits ? logits : at<float>(ws, p.logits), topk_ids, topk_w,
-                                     expert_offsets, sorted_routes, route_pos, nullptr, ws, st);
-  return check_hip(e, "route launch");
-}
-
-int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const float* bias,
-                      int32_t T, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
-  g_err[0] = 0;
-  const Layer* L = reinterpret_cast<const Layer*>(layer);
+int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* x,
+                        const uint16_t* wr, const float* bias, int32_t T, void* y, int y_dtype,
+                        void* ws, size_t ws_bytes, void* stream) {
   WsPlan p;
   GemmPlan gp;
   int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
   if (rc) return rc;
   if (y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F32)
     return set_error(MOE_EINVAL, "bad y_dtype %d", y_dtype);
+  if (accumulate && y_dtype != MOE_DTYPE_F32)
+    return set_error(MOE_EINVAL, "accumulating needs an fp32 y");
   if (T == 0) return MOE_OK;
   if (!y || !aligned(y, 16)) return set_error(MOE_EINVAL, "y must be non-null and 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Stages st{L, s, true};
   const bool prefill = gp.kind == kGemmPrefill;
-  hipError_t e = enqueue_route(*L, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
+  hipError_t e = enqueue_route(*L, wave, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
                                at<int32_t>(ws, p.ids), at<float>(ws, p.weights),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
                                at<int32_t>(ws, p.pos), prefill ? nullptr : at<float>(ws, p.r13),
@@ -407,10 +455,56 @@ int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, 
   }
   if (e != hipSuccess) return check_hip(e, "down GEMM launch");
   st.rec(5);
-  e = launch_combine(at<float>(ws, p.rows), at<int32_t>(ws, p.pos), T, L->H, L->k, y, y_dtype, s);
+  e = launch_combine(at<float>(ws, p.rows), at<int32_t>(ws, p.pos), at<int32_t>(ws, p.ids),
+                     wave.slot_map, T, L->H, L->k, y, y_dtype, accumulate, s);
   if (e != hipSuccess) return check_hip(e, "combine launch");
   st.rec(6);
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const float* bias,
+              int32_t T, int32_t* topk_ids, float* topk_w, float* logits, int32_t* expert_offsets,
+              int32_t* sorted_routes, int32_t* route_pos, void* ws, size_t ws_bytes,
+              void* stream) {
+  g_err[0] = 0;
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  WsPlan p;
+  GemmPlan gp;
+  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
+  if (rc) return rc;
+  if (!expert_offsets || (T > 0 && (!topk_ids || !topk_w || !sorted_routes || !route_pos)))
+    return set_error(MOE_EINVAL, "null output pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0)
+    return check_hip(hipMemsetAsync(expert_offsets, 0, sizeof(int32_t) * (L->E + 1), s),
+                     "hipMemsetAsync(offsets)");
+  const Stages st{L, s, false};
+  const hipError_t e = enqueue_route(*L, WaveMap{nullptr, nullptr}, p, gp, x, wr, bias, T,
+                                     logits ? logits : at<float>(ws, p.logits), topk_ids, topk_w,
+                                     expert_offsets, sorted_routes, route_pos, nullptr, ws, st);
+  return check_hip(e, "route launch");
+}
+
+int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const float* bias,
+                      int32_t T, void* y, int y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  return forward_impl(reinterpret_cast<const Layer*>(layer), WaveMap{nullptr, nullptr}, false, x,
+                      wr, bias, T, y, y_dtype, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_wave(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
+                           const float* bias, int32_t T, void* y, int y_dtype, int accumulate,
+                           void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  if (accumulate != 0 && accumulate != 1) return set_error(MOE_EINVAL, "accumulate must be 0 or 1");
+  return forward_impl(L, WaveMap{L->slot_map, L->slots}, accumulate == 1, x, wr, bias, T, y,
+                      y_dtype, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -379,16 +379,21 @@ hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s) {
 }
 
 
-// Sum of a token's k weighted rows in ascending expert order, fp32.
-template <bool BF16_OUT>
+// Sum of a token's k weighted rows in ascending expert order, fp32.  With a
+// slot map (wave mode) routes of experts mapped to the sentinel are skipped,
+// and with ACC the sum is added to y (fp32 only).
+template <bool BF16_OUT, bool ACC>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
-                                                      const int32_t* __restrict__ pos, int T,
+                                                      const int32_t* __restrict__ pos,
+                                                      const int32_t* __restrict__ ids,
+                                                      const int32_t* __restrict__ slot_map, int T,
                                                       int H, int k, void* __restrict__ y) {
   const int t = blockIdx.y;
   const int h4 = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (h4 >= H) return;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
+    if (slot_map && slot_map[ids[t * k + j]] < 0) continue;
     const float4 v = *reinterpret_cast<const float4*>(rows + (size_t)pos[t * k + j] * H + h4);
     s.x += v.x;
     s.y += v.y;
@@ -400,7 +405,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const uint32_t hi = f32_to_bf16_rne(s.z) | (f32_to_bf16_rne(s.w) << 16);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * H + h4) = make_uint2(lo, hi);
   } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * H + h4) = s;
+    float4* yp = reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * H + h4);
+    if constexpr (ACC) {
+      const float4 o = *yp;
+      s = make_float4(o.x + s.x, o.y + s.y, o.z + s.z, o.w + s.w);
+    }
+    *yp = s;
   }
 }
 
@@ -457,13 +467,19 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   return launch_decode<4, false>(a, max_tiles, s);
 }
 
-hipError_t launch_combine(const float* rows, const int32_t* pos, int T, int H, int k, void* y,
-                          int y_dtype, hipStream_t s) {
+hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
+                          const int32_t* slot_map, int T, int H, int k, void* y, int y_dtype,
+                          bool accumulate, hipStream_t s) {
   const dim3 grid((H / 4 + 255) / 256, T);
   if (y_dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, rows, pos, T, H, k, y);
+    hipLaunchKernelGGL((combine_kernel<true, false>), grid, dim3(256), 0, s, rows, pos, ids, slot_map,
+                       T, H, k, y);
+  else if (accumulate)
+    hipLaunchKernelGGL((combine_kernel<false, true>), grid, dim3(256), 0, s, rows, pos, ids, slot_map,
+                       T, H, k, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, rows, pos, T, H, k, y);
+    hipLaunchKernelGGL((combine_kernel<false, false>), grid, dim3(256), 0, s, rows, pos, ids,
+                       slot_map, T, H, k, y);
   return hipGetLastError();
 }
 

@@ -62,8 +62,22 @@ struct WsPlan {
 struct Layer {
   int32_t H, I, E, k;
   DevHandle* table;      // device [E]
+  // wave execution: resident slots (up to E) and the global-expert-to-slot
+  // map (-1 = inactive sentinel), both stream-ordered device state; slot_set
+  // records on the host which slots hold a validated handle
+  DevHandle* slots;      // device [E]
+  int32_t* slot_map;     // device [E]
+  uint8_t* slot_set;     // host [E]
   void* stage_events[7];
   int32_t n_stage_events;
+};
+
+// Wave mode of one forward: expert e runs from slots[slot_map[e]] when that
+// is >= 0 and contributes nothing otherwise.  Both null: every expert runs
+// from the layer's handle table.
+struct WaveMap {
+  const int32_t* slot_map;
+  const DevHandle* slots;
 };
 
 // error state ---------------------------------------------------------------
@@ -77,6 +91,7 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp);
 // launchers (return hipError_t of the launch) --------------------------------
 hipError_t launch_quantize_pack(int tier, int layout, const uint16_t* w, int64_t n, int64_t k,
                                 uint8_t* dst, int* err_flag, hipStream_t s);
+hipError_t launch_set_slot_map(int32_t* map, const int32_t* host_map, int E, hipStream_t s);
 hipError_t launch_set_handles(DevHandle* table, int first, int count,
                               const moe_expert_handle* h, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
@@ -86,10 +101,11 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 // Grouping: one workgroup for T <= kPermSmallT, else a rank pass and a
 // scatter pass over blocks of kPermChunk tokens (rank [T*k] and chunk_counts
 // [ceil(T / kPermChunk) * E] are workspace).
-hipError_t launch_permute(const DevHandle* table, const int32_t* ids, int T, int k, int E,
-                          int32_t* offsets, int32_t* sorted, int32_t* pos, TileEntry* tiles13,
-                          int32_t* ntiles13, int bm13, TileEntry* tiles2, int32_t* ntiles2, int bm2,
-                          int32_t* rank, int32_t* chunk_counts, hipStream_t s);
+hipError_t launch_permute(const DevHandle* table, WaveMap wave, const int32_t* ids, int T, int k,
+                          int E, int32_t* offsets, int32_t* sorted, int32_t* pos,
+                          TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
+                          int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,
+                          hipStream_t s);
 hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16_t* x,
                          const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
                          int max_tiles, const float* r13, uint16_t* act, float* r2,
@@ -103,7 +119,10 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream
 hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
                           uint16_t* act16, const float* topk_w, float* rows, hipStream_t s);
-hipError_t launch_combine(const float* rows, const int32_t* pos, int T, int H, int k, void* y,
-                          int y_dtype, hipStream_t s);
+// y[t] (=|+=) sum over the token's routes in ascending expert order; with a
+// slot map, routes whose expert maps to the sentinel are skipped.
+hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
+                          const int32_t* slot_map, int T, int H, int k, void* y, int y_dtype,
+                          bool accumulate, hipStream_t s);
 
 }  // namespace moe

@@ -29,6 +29,7 @@ from .moe_oracle import (  # noqa: F401
     permutation,
     expert_ffn,
     layer_forward,
+    wave_forward,
     route,
     OracleLayer,
 )

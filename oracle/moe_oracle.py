@@ -346,6 +346,30 @@ def layer_forward(x_bf16: np.ndarray, routing: Dict[str, np.ndarray],
     return out.astype(np.float32)
 
 
+def wave_forward(x_bf16: np.ndarray, routing: Dict[str, np.ndarray],
+                 get_expert: Callable[[int], OracleExpert], active) -> np.ndarray:
+    """One wave of [ExactMoE] §3.4: the layer output restricted to the routes
+    whose expert is in `active` (the experts mapped to a resident slot; every
+    other expert maps to the inactive sentinel and contributes nothing).  The
+    router weights are the full top-k softmax, not renormalized within the
+    wave, so the waves of a partition of the experts sum to layer_forward.
+    """
+    x = bf16_bits_to_f32(x_bf16).astype(np.float64)
+    ids, w = routing["ids"], routing["weights"].astype(np.float64)
+    T, k = ids.shape
+    H = x.shape[1]
+    members = set(int(e) for e in active)
+    out = np.zeros((T, H), dtype=np.float64)
+    for j in range(k):                            # slots ascending by expert
+        for e in np.unique(ids[:, j]):
+            if int(e) not in members:
+                continue
+            ex = get_expert(int(e))
+            rows = np.nonzero(ids[:, j] == e)[0]
+            out[rows] += w[rows, j][:, None] * expert_ffn(x[rows], ex.wg_hat, ex.wu_hat, ex.wd_hat)
+    return out.astype(np.float32)
+
+
 class OracleLayer:
     """A layer's geometry, tier table and lazily built dequantized experts."""
 

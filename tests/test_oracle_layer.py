@@ -132,6 +132,27 @@ def test_wave_additivity():
     assert not np.allclose(y, 0)
 
 
+def test_wave_forward_partition_sums_to_layer():
+    """wave_forward over a partition of the experts: the waves sum to the full
+    output, an empty wave is zero, and a wave holding every expert equals it."""
+    layer, x, wr = _layer_and_inputs()
+    y, r = layer.forward(x, wr)
+    rng = np.random.default_rng(9)
+    waves = np.array_split(rng.permutation(layer.E), 4)
+    total = sum(oracle.wave_forward(x, r, layer.expert, w).astype(np.float64) for w in waves)
+    rms = np.sqrt(np.mean(y.astype(np.float64) ** 2))
+    assert np.max(np.abs(total - y)) <= 1e-6 * rms
+    assert not np.any(oracle.wave_forward(x, r, layer.expert, []))
+    full = oracle.wave_forward(x, r, layer.expert, range(layer.E))
+    assert np.max(np.abs(full - y)) <= 1e-6 * rms
+    # a one-expert wave holds exactly that expert's weighted rows
+    e0 = int(r["ids"][0, 0])
+    one = oracle.wave_forward(x, r, layer.expert, [e0])
+    rows = np.nonzero((r["ids"] == e0).any(axis=1))[0]
+    others = np.setdiff1d(np.arange(x.shape[0]), rows)
+    assert not np.any(one[others]) and np.all(np.any(one[rows] != 0, axis=1))
+
+
 def test_token_permutation_equivariance():
     layer, x, wr = _layer_and_inputs(24)
     y, _ = layer.forward(x, wr)
