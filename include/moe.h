@@ -128,6 +128,16 @@ size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in);
 int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_out,
                       int64_t k_in, void* dst, size_t dst_bytes, void* stream);
 
+/* Stream-ordered quantize and pack (same operation, arguments and layout as
+ * moe_quantize_pack) for repacking while forwards run: it only enqueues work on
+ * `stream` (no allocation, no synchronization).  status: device int32, written
+ * 0 when the pack starts and nonzero when it ends if a weight is non-finite or a
+ * scale overflows fp16 (dst is then unspecified); read it after the stream
+ * work completes. */
+int moe_quantize_pack_async(int tier, int layout, const uint16_t* w_bf16, int64_t n_out,
+                            int64_t k_in, void* dst, size_t dst_bytes, int32_t* status,
+                            void* stream);
+
 /* Create a layer.  table: host array of n_experts handles, copied into a
  * library-owned device table on `stream` (stream-ordered).  The layer object
  * is owned by the caller until moe_layer_destroy. */
@@ -161,6 +171,33 @@ int moe_layer_set_experts(moe_layer_t layer, int32_t first, int32_t count,
 int moe_layer_set_slots(moe_layer_t layer, int32_t first, int32_t count,
                         const moe_expert_handle* handles, void* stream);
 int moe_layer_set_slot_map(moe_layer_t layer, const int32_t* expert_to_slot, void* stream);
+
+/* DynaExq (abstract): expert hotness is estimated from router traces over a
+ * long horizon; a budget-feasible top-n rule picks the per-layer set kept at
+ * high precision; promotions and demotions go through stable handles
+ * (moe_layer_set_experts) so every forward runs on fully materialized experts.
+ *
+ * moe_layer_set_hotness: from the next call on, every moe_layer_forward (and
+ * every moe_layer_forward_wave with accumulate = 0, i.e. once per layer call)
+ * updates hot[e] = decay * hot[e] + (routes to expert e in that call), on the
+ * call's stream, in its grouping kernel.  hot: caller-owned device float
+ * [n_experts], initialized by the caller; NULL turns the update off.
+ * decay in [0, 1] (1: plain counts). */
+int moe_layer_set_hotness(moe_layer_t layer, float* hot, float decay);
+
+/* Budget-feasible top-n tier plan (host only, no GPU work).
+ *   hot             host float [n_experts]: hotness (no NaN).
+ *   bytes_per_tier  host size_t [3]: bytes of one expert (gate/up + down
+ *                   blobs) in tier 0 (bf16), 1 (int8), 2 (int4).
+ *   budget_bytes    bytes the layer's experts may occupy.
+ * Experts are ranked by hotness (descending, ties to the lower id); the n
+ * hottest get hi_tier and the rest lo_tier, n the largest value with
+ * n * bytes[hi] + (n_experts - n) * bytes[lo] <= budget_bytes.
+ * tiers_out: host int32 [n_experts]; n_hi_out (may be NULL) receives n.
+ * MOE_ENOSPC if even all experts at lo_tier exceed the budget. */
+int moe_plan_tiers(const float* hot, int32_t n_experts, const size_t* bytes_per_tier,
+                   size_t budget_bytes, int32_t hi_tier, int32_t lo_tier, int32_t* tiers_out,
+                   int32_t* n_hi_out);
 
 /* Free the layer's device state.  The caller must have synchronized every
  * stream that has work using the layer. */

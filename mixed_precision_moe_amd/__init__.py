@@ -17,5 +17,8 @@ from .api import (  # noqa: F401
     Layer,
     pack_expert,
     packed_size,
+    plan_tiers,
     quantize_pack,
+    quantize_pack_async,
 )
+from .dynaexq import DynaExq  # noqa: F401

@@ -21,8 +21,9 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = (
-    "moe_packed_size", "moe_quantize_pack", "moe_layer_create", "moe_layer_set_experts",
-    "moe_layer_set_slots", "moe_layer_set_slot_map", "moe_layer_destroy", "moe_workspace_size",
+    "moe_packed_size", "moe_quantize_pack", "moe_quantize_pack_async", "moe_layer_create",
+    "moe_layer_set_experts", "moe_layer_set_slots", "moe_layer_set_slot_map",
+    "moe_layer_set_hotness", "moe_plan_tiers", "moe_layer_destroy", "moe_workspace_size",
     "moe_route", "moe_layer_forward", "moe_layer_forward_wave", "moe_layer_set_stage_events",
     "moe_strerror", "moe_last_error", "moe_abi_version",
 )
@@ -63,6 +64,11 @@ def load() -> ctypes.CDLL:
         "moe_layer_create": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.POINTER(ExpertHandle),
                                             vp, ctypes.POINTER(vp)]),
         "moe_layer_set_experts": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(ExpertHandle), vp]),
+        "moe_quantize_pack_async": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, vp, i64, i64, vp, sz,
+                                                   vp, vp]),
+        "moe_layer_set_hotness": (ctypes.c_int, [vp, vp, ctypes.c_float]),
+        "moe_plan_tiers": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(sz), sz,
+                                          i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "moe_layer_set_slots": (ctypes.c_int, [vp, i32, i32, ctypes.POINTER(ExpertHandle), vp]),
         "moe_layer_set_slot_map": (ctypes.c_int, [vp, ctypes.POINTER(i32), vp]),
         "moe_layer_destroy": (ctypes.c_int, [vp]),

@@ -63,6 +63,32 @@ def quantize_pack(w: torch.Tensor, tier: int, layout: int = LAYOUT_PLAIN,
     return out
 
 
+def quantize_pack_async(w: torch.Tensor, tier: int, layout: int, out: torch.Tensor,
+                        status: torch.Tensor, stream=None) -> torch.Tensor:
+    """Enqueue quantize+pack on `stream` without synchronizing; status (device
+    int32 [1]) is nonzero after completion if the weights were out of range."""
+    _require_cuda(w, "w", _BF16)
+    _require_cuda(status, "status", (torch.int32,))
+    n, k = w.shape
+    check(_lib.load().moe_quantize_pack_async(tier, layout, w.data_ptr(), n, k, out.data_ptr(),
+                                              out.numel(), status.data_ptr(), _stream(stream)),
+          "moe_quantize_pack_async")
+    return out
+
+
+def plan_tiers(hot: Sequence[float], bytes_per_tier: Sequence[int], budget_bytes: int,
+               hi_tier: int, lo_tier: int) -> Tuple[List[int], int]:
+    """Budget-feasible top-n plan (host): (tier per expert, n promoted)."""
+    E = len(hot)
+    h = (ctypes.c_float * E)(*[float(v) for v in hot])
+    b = (ctypes.c_size_t * 3)(*[int(v) for v in bytes_per_tier])
+    out = (ctypes.c_int32 * E)()
+    n = ctypes.c_int32()
+    check(_lib.load().moe_plan_tiers(h, E, b, int(budget_bytes), hi_tier, lo_tier, out,
+                                     ctypes.byref(n)), "moe_plan_tiers")
+    return list(out), n.value
+
+
 def pack_expert(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, tier: int,
                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """(w13 blob, w2 blob) of one expert from its bf16 [I,H], [I,H], [H,I] weights."""
@@ -183,6 +209,15 @@ class Layer:
                 check(rc, "moe_layer_forward")
             return keep
         return run
+
+    def set_hotness(self, hot: Optional[torch.Tensor], decay: float = 1.0) -> None:
+        """Route-count trace of later forwards: hot[e] = decay*hot[e] + routes to e."""
+        if hot is not None:
+            _require_cuda(hot, "hot", (torch.float32,))
+            if hot.numel() != self.n_experts:
+                raise ValueError("hot needs one entry per expert")
+        check(self._lib.moe_layer_set_hotness(self._h, _ptr(hot), float(decay)), "moe_layer_set_hotness")
+        self._hot = hot
 
     def set_slots(self, first: int, handles, stream=None) -> None:
         """Resident slots [first, first+len) for wave execution; handles as for

@@ -172,9 +172,8 @@ size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in) {
   return round_up(bytes, kBlobAlign);
 }
 
-int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_out, int64_t k_in,
-                      void* dst, size_t dst_bytes, void* stream) {
-  g_err[0] = 0;
+static int check_pack_args(int tier, int layout, const uint16_t* w_bf16, int64_t n_out,
+                           int64_t k_in, void* dst, size_t dst_bytes, size_t* need, size_t* payload) {
   if (tier < MOE_TIER_BF16 || tier > MOE_TIER_INT4)
     return set_error(MOE_EINVAL, "bad tier %d", tier);
   if (layout != MOE_LAYOUT_PLAIN && layout != MOE_LAYOUT_GATE_UP)
@@ -188,20 +187,28 @@ int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_ou
                      (long long)n_out, (long long)k_in);
   if ((uint64_t)n_out * (uint64_t)k_in * 2 > 0xffffffffull)
     return set_error(MOE_ESHAPE, "a packed matrix must stay below 4 GiB");
-  const size_t need = moe_packed_size(tier, n_out, k_in);
-  if (dst_bytes < need)
-    return set_error(MOE_ENOSPC, "dst has %zu bytes, %zu needed", dst_bytes, need);
+  *need = moe_packed_size(tier, n_out, k_in);
+  if (dst_bytes < *need)
+    return set_error(MOE_ENOSPC, "dst has %zu bytes, %zu needed", dst_bytes, *need);
+  switch (tier) {
+    case MOE_TIER_INT4: *payload = (size_t)n_out * k_in / 2 + (size_t)n_out * (k_in / kGroup) * 2; break;
+    case MOE_TIER_INT8: *payload = (size_t)n_out * k_in + 2 * (size_t)n_out; break;
+    default: *payload = 2 * (size_t)n_out * k_in; break;
+  }
+  return MOE_OK;
+}
+
+int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_out, int64_t k_in,
+                      void* dst, size_t dst_bytes, void* stream) {
+  g_err[0] = 0;
+  size_t need = 0, payload = 0;
+  int rc = check_pack_args(tier, layout, w_bf16, n_out, k_in, dst, dst_bytes, &need, &payload);
+  if (rc) return rc;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int* flag = nullptr;
-  int rc = check_hip(hipMalloc(&flag, sizeof(int)), "hipMalloc(flag)");
+  rc = check_hip(hipMalloc(&flag, sizeof(int)), "hipMalloc(flag)");
   if (rc) return rc;
   int host_flag = 0;
-  size_t payload;
-  switch (tier) {
-    case MOE_TIER_INT4: payload = (size_t)n_out * k_in / 2 + (size_t)n_out * (k_in / kGroup) * 2; break;
-    case MOE_TIER_INT8: payload = (size_t)n_out * k_in + 2 * (size_t)n_out; break;
-    default: payload = 2 * (size_t)n_out * k_in; break;
-  }
   if (!rc) rc = check_hip(hipMemsetAsync(flag, 0, sizeof(int), s), "hipMemsetAsync(flag)");
   if (!rc && need > payload)
     rc = check_hip(hipMemsetAsync(static_cast<uint8_t*>(dst) + payload, 0, need - payload, s),
@@ -218,6 +225,23 @@ int moe_quantize_pack(int tier, int layout, const uint16_t* w_bf16, int64_t n_ou
   if (!rc && host_flag)
     rc = set_error(MOE_ERANGE, "non-finite weight or fp16 scale overflow");
   return rc;
+}
+
+int moe_quantize_pack_async(int tier, int layout, const uint16_t* w_bf16, int64_t n_out,
+                            int64_t k_in, void* dst, size_t dst_bytes, int32_t* status,
+                            void* stream) {
+  g_err[0] = 0;
+  size_t need = 0, payload = 0;
+  int rc = check_pack_args(tier, layout, w_bf16, n_out, k_in, dst, dst_bytes, &need, &payload);
+  if (rc) return rc;
+  if (!status || !aligned(status, 4)) return set_error(MOE_EINVAL, "status must be a 4-byte aligned device int");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_fill_zero(status, sizeof(int32_t), s);
+  if (e == hipSuccess && need > payload)   // payload and need are multiples of 4
+    e = launch_fill_zero(static_cast<uint8_t*>(dst) + payload, need - payload, s);
+  if (e == hipSuccess)
+    e = launch_quantize_pack(tier, layout, w_bf16, n_out, k_in, static_cast<uint8_t*>(dst), status, s);
+  return check_hip(e, "quantize_pack launch");
 }
 
 int moe_layer_create(const moe_layer_desc* d, const moe_expert_handle* table, void* stream,
@@ -244,6 +268,8 @@ int moe_layer_create(const moe_layer_desc* d, const moe_expert_handle* table, vo
   L->k = d->top_k;
   L->n_stage_events = 0;
   L->table = nullptr;
+  L->hot = nullptr;
+  L->hot_decay = 1.0f;
   L->slots = nullptr;
   L->slot_map = nullptr;
   L->slot_set = new (std::nothrow) uint8_t[L->E]();
@@ -316,6 +342,58 @@ int moe_layer_set_slot_map(moe_layer_t layer, const int32_t* expert_to_slot, voi
                    "set_slot_map launch");
 }
 
+int moe_layer_set_hotness(moe_layer_t layer, float* hot, float decay) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  if (!(decay >= 0.0f && decay <= 1.0f)) return set_error(MOE_EINVAL, "decay must be in [0, 1]");
+  if (hot && !aligned(hot, 4)) return set_error(MOE_EINVAL, "hot must be 4-byte aligned");
+  L->hot = hot;
+  L->hot_decay = decay;
+  return MOE_OK;
+}
+
+int moe_plan_tiers(const float* hot, int32_t n_experts, const size_t* bytes_per_tier,
+                   size_t budget_bytes, int32_t hi_tier, int32_t lo_tier, int32_t* tiers_out,
+                   int32_t* n_hi_out) {
+  g_err[0] = 0;
+  if (!hot || !bytes_per_tier || !tiers_out) return set_error(MOE_EINVAL, "null pointer");
+  if (n_experts < 1 || n_experts > kMaxExperts)
+    return set_error(MOE_ESHAPE, "n_experts must be in [1, %d]", kMaxExperts);
+  if (hi_tier < MOE_TIER_BF16 || hi_tier > MOE_TIER_INT4 || lo_tier < MOE_TIER_BF16 ||
+      lo_tier > MOE_TIER_INT4)
+    return set_error(MOE_EINVAL, "bad tier");
+  for (int e = 0; e < n_experts; ++e)
+    if (!(hot[e] == hot[e])) return set_error(MOE_EINVAL, "hotness of expert %d is NaN", e);
+  const size_t lo = bytes_per_tier[lo_tier], hi = bytes_per_tier[hi_tier];
+  if (lo > budget_bytes / (size_t)n_experts || (size_t)n_experts * lo > budget_bytes)
+    return set_error(MOE_ENOSPC, "%d experts at the low tier need %zu bytes, budget %zu", n_experts,
+                     (size_t)n_experts * lo, budget_bytes);
+  // top-n: experts ranked by hotness (descending, ties to the lower id); the
+  // n hottest take the high tier, n the largest that fits the budget
+  int order[kMaxExperts];
+  for (int e = 0; e < n_experts; ++e) order[e] = e;
+  for (int i = 1; i < n_experts; ++i) {   // insertion sort: stable, so ties keep the lower id first
+    const int e = order[i];
+    int j = i - 1;
+    while (j >= 0 && hot[order[j]] < hot[e]) {
+      order[j + 1] = order[j];
+      --j;
+    }
+    order[j + 1] = e;
+  }
+  const size_t spare = budget_bytes - (size_t)n_experts * lo;
+  int n_hi = 0;
+  if (hi <= lo)
+    n_hi = n_experts;
+  else
+    n_hi = (int)((spare / (hi - lo)) < (size_t)n_experts ? spare / (hi - lo) : (size_t)n_experts);
+  for (int e = 0; e < n_experts; ++e) tiers_out[e] = lo_tier;
+  for (int i = 0; i < n_hi; ++i) tiers_out[order[i]] = hi_tier;
+  if (n_hi_out) *n_hi_out = n_hi;
+  return MOE_OK;
+}
+
 int moe_layer_destroy(moe_layer_t layer) {
   g_err[0] = 0;
   Layer* L = reinterpret_cast<Layer*>(layer);
@@ -386,7 +464,7 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
 }
 
-hipError_t enqueue_route(const Layer& L, WaveMap wave, const WsPlan& p, const GemmPlan& gp, const uint16_t* x,
+hipError_t enqueue_route(const Layer& L, WaveMap wave, Hotness hotness, const WsPlan& p, const GemmPlan& gp, const uint16_t* x,
                          const uint16_t* wr, const float* bias, int T, float* logits,
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos,
                          float* r13, void* ws, const Stages& st) {
@@ -397,7 +475,7 @@ hipError_t enqueue_route(const Layer& L, WaveMap wave, const WsPlan& p, const Ge
   e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
   if (e != hipSuccess) return e;
   st.rec(2);
-  return launch_permute(L.table, wave, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
+  return launch_permute(L.table, wave, hotness, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
                         at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
                         at<int32_t>(ws, p.ntiles2), gp.bm2, at<int32_t>(ws, p.rank),
                         at<int32_t>(ws, p.chunk_counts), st.s);
@@ -423,7 +501,10 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Stages st{L, s, true};
   const bool prefill = gp.kind == kGemmPrefill;
-  hipError_t e = enqueue_route(*L, wave, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
+  // the hotness trace counts each layer call once: a plain forward, or the
+  // first wave of a layer call (the one that does not accumulate)
+  const Hotness hotness{accumulate ? nullptr : L->hot, L->hot_decay};
+  hipError_t e = enqueue_route(*L, wave, hotness, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
                                at<int32_t>(ws, p.ids), at<float>(ws, p.weights),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
                                at<int32_t>(ws, p.pos), prefill ? nullptr : at<float>(ws, p.r13),
@@ -483,7 +564,8 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const fl
     return check_hip(hipMemsetAsync(expert_offsets, 0, sizeof(int32_t) * (L->E + 1), s),
                      "hipMemsetAsync(offsets)");
   const Stages st{L, s, false};
-  const hipError_t e = enqueue_route(*L, WaveMap{nullptr, nullptr}, p, gp, x, wr, bias, T,
+  const hipError_t e = enqueue_route(*L, WaveMap{nullptr, nullptr}, Hotness{nullptr, 1.0f}, p, gp,
+                                     x, wr, bias, T,
                                      logits ? logits : at<float>(ws, p.logits), topk_ids, topk_w,
                                      expert_offsets, sorted_routes, route_pos, nullptr, ws, st);
   return check_hip(e, "route launch");

@@ -68,6 +68,10 @@ struct Layer {
   DevHandle* slots;      // device [E]
   int32_t* slot_map;     // device [E]
   uint8_t* slot_set;     // host [E]
+  // long-horizon hotness: each forward sets hot[e] = decay * hot[e] + its
+  // routes to e (caller-owned device [E], or null)
+  float* hot;
+  float hot_decay;
   void* stage_events[7];
   int32_t n_stage_events;
 };
@@ -80,6 +84,12 @@ struct WaveMap {
   const DevHandle* slots;
 };
 
+// Per-forward hotness update of the grouping kernels (hot null: none).
+struct Hotness {
+  float* hot;
+  float decay;
+};
+
 // error state ---------------------------------------------------------------
 int set_error(int status, const char* fmt, ...);
 int check_hip(hipError_t e, const char* what);
@@ -89,6 +99,9 @@ GemmPlan plan_gemm(const Layer& L, int T);
 WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp);
 
 // launchers (return hipError_t of the launch) --------------------------------
+// Zero bytes [p, p + bytes) with a kernel (bytes a multiple of 4; usable
+// where a memset node is not wanted).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_quantize_pack(int tier, int layout, const uint16_t* w, int64_t n, int64_t k,
                                 uint8_t* dst, int* err_flag, hipStream_t s);
 hipError_t launch_set_slot_map(int32_t* map, const int32_t* host_map, int E, hipStream_t s);
@@ -101,7 +114,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 // Grouping: one workgroup for T <= kPermSmallT, else a rank pass and a
 // scatter pass over blocks of kPermChunk tokens (rank [T*k] and chunk_counts
 // [ceil(T / kPermChunk) * E] are workspace).
-hipError_t launch_permute(const DevHandle* table, WaveMap wave, const int32_t* ids, int T, int k,
+hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness, const int32_t* ids, int T, int k,
                           int E, int32_t* offsets, int32_t* sorted, int32_t* pos,
                           TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
                           int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,

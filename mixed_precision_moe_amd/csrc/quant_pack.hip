@@ -186,7 +186,21 @@ __global__ __launch_bounds__(256) void pack_bf16(const uint16_t* __restrict__ w,
   if (bad) atomicOr(err, 1);
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, size_t n_words) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_words; i += (size_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  if (words == 0) return hipSuccess;
+  const size_t blocks = (words + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
+                     s, static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_pack(int tier, int layout, const uint16_t* w, int64_t n, int64_t k,
                                 uint8_t* dst, int* err_flag, hipStream_t s) {

@@ -235,10 +235,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
 // carrying the expert's tier and packed weights from the handle table (or, in
 // wave mode, from its resident slot).
 __device__ __forceinline__ void write_tile_tables(const DevHandle* table, WaveMap wave,
-                                                  const int* off, int E, TileEntry* tiles13,
-                                                  int32_t* ntiles13, int bm13, TileEntry* tiles2,
-                                                  int32_t* ntiles2, int bm2, int* scan) {
+                                                  Hotness hotness, const int* off, int E,
+                                                  TileEntry* tiles13, int32_t* ntiles13, int bm13,
+                                                  TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                                                  int* scan) {
   const int tid = threadIdx.x;
+  // DynaExq hotness from the router trace: decayed count of routes per expert
+  if (hotness.hot && tid < E)
+    hotness.hot[tid] = hotness.decay * hotness.hot[tid] + (float)(off[tid + 1] - off[tid]);
   const int e = min(tid, E - 1);
   // wave mode: only experts mapped to a resident slot get tiles, with the
   // slot's weights (ExactMoE 3.4: the other experts map to the sentinel)
@@ -276,7 +280,7 @@ __device__ __forceinline__ void write_tile_tables(const DevHandle* table, WaveMa
 // Finally the M-tile tables of both grouped GEMMs are written, each entry
 // carrying the expert's tier and packed weights from the handle table.
 __global__ __launch_bounds__(1024) void permute_kernel(
-    const DevHandle* __restrict__ table, WaveMap wmap, const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
+    const DevHandle* __restrict__ table, WaveMap wmap, Hotness hotness, const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
     int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
     int32_t* __restrict__ ntiles2, int bm2) {
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
   __syncthreads();
 
-  write_tile_tables(table, wmap, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+  write_tile_tables(table, wmap, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
 }
 
 // Rank pass of the multi-block grouping (large T).  Block c owns the 256
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
 // offset + base + rank: the stable order by (expert, token).  Block 0 also
 // writes the offsets and the M-tile tables.
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(
-    const DevHandle* __restrict__ table, WaveMap wmap, const int32_t* __restrict__ ids, int T, int k, int E,
+    const DevHandle* __restrict__ table, WaveMap wmap, Hotness hotness, const int32_t* __restrict__ ids, int T, int k, int E,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ chunk_counts, int nchunks,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
     TileEntry* __restrict__ tiles13, int32_t* __restrict__ ntiles13, int bm13,
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   }
   if (c != 0) return;
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
-  write_tile_tables(table, wmap, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+  write_tile_tables(table, wmap, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
 }
 
 }  // namespace
@@ -444,7 +448,7 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const DevHandle* table, WaveMap wave, const int32_t* ids, int T, int k,
+hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness, const int32_t* ids, int T, int k,
                           int E, int32_t* offsets, int32_t* sorted, int32_t* pos,
                           TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
                           int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,
@@ -455,7 +459,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, const int32_t* i
                        chunk_counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(1024), 0, s, table, wave, ids, T, k, E,
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(1024), 0, s, table, wave, hotness, ids, T, k, E,
                        rank, chunk_counts, nchunks, offsets, sorted, pos, tiles13, ntiles13, bm13,
                        tiles2, ntiles2, bm2);
     return hipGetLastError();
@@ -469,7 +473,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, const int32_t* i
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, wave, ids, T, k, E, offsets, sorted,
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, wave, hotness, ids, T, k, E, offsets, sorted,
                      pos, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2);
   return hipGetLastError();
 }

@@ -30,6 +30,7 @@ from .moe_oracle import (  # noqa: F401
     expert_ffn,
     layer_forward,
     wave_forward,
+    plan_tiers,
     route,
     OracleLayer,
 )

@@ -370,6 +370,26 @@ def wave_forward(x_bf16: np.ndarray, routing: Dict[str, np.ndarray],
     return out.astype(np.float32)
 
 
+def plan_tiers(hot, bytes_per_tier, budget_bytes: int, hi_tier: int, lo_tier: int):
+    """[DynaExq] (abstract): a budget-feasible top-n rule selects the experts
+    kept at high precision.  Reading: rank experts by hotness (descending,
+    ties to the lower id); the n hottest take hi_tier, the rest lo_tier, with n
+    the largest count whose total bytes fit the budget.  Returns (tiers, n);
+    raises ValueError when all experts at lo_tier already exceed it."""
+    E = len(hot)
+    lo, hi = int(bytes_per_tier[lo_tier]), int(bytes_per_tier[hi_tier])
+    if E * lo > budget_bytes:
+        raise ValueError("budget below the all-low-tier size")
+    rank = sorted(range(E), key=lambda e: (-float(hot[e]), e))
+    n = 0
+    while n < E and (n + 1) * hi + (E - n - 1) * lo <= budget_bytes:
+        n += 1
+    tiers = [lo_tier] * E
+    for e in rank[:n]:
+        tiers[e] = hi_tier
+    return tiers, n
+
+
 class OracleLayer:
     """A layer's geometry, tier table and lazily built dequantized experts."""
 

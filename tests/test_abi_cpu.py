@@ -121,10 +121,9 @@ def test_null_layer_calls():
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):
-    """The binding has no fallback: a missing library is an import-time error."""
-    import importlib
+    """The binding has no fallback: a missing library is an import-time error.
+    (monkeypatch restores the loaded library afterwards.)"""
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
-    importlib.reload(_lib)
