@@ -158,6 +158,57 @@ def stored_traffic(workload_key, path_kind):
     return d.get("traffic_bytes")
 
 
+def compare_sequential(layer, x, wr, bias, ids, T, H, dev, fused_fwd, reps):
+    """The layer-level comparison the ExactMoE page makes (sequential per-expert
+    execution vs one fused grouped forward), on MI355X: the same layer, the
+    same tokens, either one fused forward, or one wave per touched expert (the
+    slot map sends only that expert to its slot; the first wave routes, the
+    others keep its routing and accumulate).  Both are host-launched and timed
+    with events; the accumulated output is checked against the fused one."""
+    import torch
+    touched = sorted(set(int(e) for e in np.unique(ids)))
+    E = layer.n_experts
+    layer.set_slots(0, layer.handles)            # slot e holds expert e
+    maps = []
+    for e in touched:
+        m = [-1] * E
+        m[e] = e
+        maps.append(m)
+    y_seq = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = layer.workspace(T, dev)
+
+    def sequential():
+        for i, m in enumerate(maps):
+            layer.set_slot_map(m)
+            layer.forward_wave(x, wr, bias, y=y_seq, accumulate=i > 0, workspace=ws)
+
+    y_fused = layer.forward(x, wr, bias, out_dtype=torch.float32)
+    sequential()
+    torch.cuda.synchronize()
+    gap = float((y_seq - y_fused).abs().max() / y_fused.pow(2).mean().sqrt())
+    times = {}
+    for name, fn in (("fused", fused_fwd), ("sequential", sequential)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        times[name] = a.elapsed_time(b) / reps
+    log(f"[bench] fused {times['fused']:.3f} ms, sequential over {len(touched)} experts "
+        f"{times['sequential']:.3f} ms; outputs agree to {gap:.1e} x RMS")
+    return {"fused_ms_per_layer": round(times["fused"], 4),
+            "sequential_ms_per_layer": round(times["sequential"], 4),
+            "fused_speedup": round(times["sequential"] / times["fused"], 2),
+            "experts_run_one_at_a_time": len(touched),
+            "max_abs_gap_over_rms": gap,
+            "launch": "host launch per call, both",
+            "sequential_kind": "one wave per touched expert: slot-map update, regroup, gate/up GEMM, "
+                               "down GEMM, accumulate"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +221,9 @@ def main():
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--eager", action="store_true",
                     help="launch each forward from the host instead of replaying a HIP graph")
+    ap.add_argument("--compare-sequential", action="store_true",
+                    help="also time the same layer run one expert at a time (per-expert waves "
+                         "through the slot map) against the fused grouped forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run plain device copies of this many MiB (for scaling HBM "
                          "counters) and exit")
@@ -318,6 +372,9 @@ def main():
         },
         "roofline": roof,
     }
+    if args.compare_sequential:
+        out["comparison"] = compare_sequential(layers[0], x, wr, bias, ids, T, cfg.hidden, dev,
+                                               fwd[0], max(5, min(args.steps, 50)))
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(cfg, tiers, x_np, wr_np, bias_np)

@@ -204,7 +204,9 @@ int moe_plan_tiers(const float* hot, int32_t n_experts, const size_t* bytes_per_
 int moe_layer_destroy(moe_layer_t layer);
 
 /* Bytes of device workspace a route or forward call with T tokens needs.
- * The workspace is scratch: no state is kept in it between calls. */
+ * The workspace is scratch: no state is kept in it between calls, except that
+ * a moe_layer_forward_wave with accumulate = 1 reads the routing left by the
+ * preceding wave of the same layer call. */
 size_t moe_workspace_size(moe_layer_t layer, int32_t T);
 
 /* Routing only (ExactMoE §3.1 and §3.4 grouping).  All pointers device.
@@ -240,11 +242,18 @@ int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
 /* One wave: as moe_layer_forward, with the router and top-k over all experts
  * unchanged (weights not renormalized within a wave), but only the experts the
  * current slot map sends to a slot contribute, each computed from its slot's
- * handle; every other route contributes nothing.  accumulate = 0: y = the
- * wave's output; accumulate = 1: y += it (y_dtype must be MOE_DTYPE_F32).
+ * handle; every other route contributes nothing.
+ *   accumulate = 0: the first wave of a layer call: routes the tokens and
+ *                   sets y = the wave's output.
+ *   accumulate = 1: a later wave of the same call: keeps the routing (top-k
+ *                   ids, weights and activation sums) that the preceding wave
+ *                   left in ws, regroups it for the current slot map and adds
+ *                   the wave's output to y (y_dtype must be MOE_DTYPE_F32).
+ *                   x, wr, bias, T and ws must be those of that first wave,
+ *                   ordered after it on the same stream.
  * Over waves whose slot maps partition the experts, the accumulated y is the
- * layer output up to fp32 rounding of the sum order.  Same pointer,
- * workspace and stream rules as moe_layer_forward. */
+ * layer output up to fp32 rounding of the sum order.  Same pointer and
+ * stream rules as moe_layer_forward. */
 int moe_layer_forward_wave(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
                            const float* bias, int32_t T, void* y, int y_dtype, int accumulate,
                            void* ws, size_t ws_bytes, void* stream);

@@ -74,6 +74,9 @@ CONFIGS: Dict[int, LayerConfig] = {
                    (32, 1, 256, 4096), 4096, n_int8=64),
     5: LayerConfig(5, "Mixtral-shaped MoE layer, prefill", 4096, 8, 2, 14336,
                    (8192,), 8192),
+    # the second model family the ExactMoE page measures (OLMoE: 64 experts,
+    # top-8); decode batch of 32 and a 512-token prefill chunk
+    6: LayerConfig(6, "OLMoE-shaped MoE layer", 2048, 64, 8, 1024, (32, 512), 512),
 }
 
 

@@ -109,6 +109,7 @@ class Layer:
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self._lib = _lib.load()
         self._blobs: List[Tuple[torch.Tensor, torch.Tensor]] = [(h[1], h[2]) for h in handles]
+        self.handles: List[Tuple[int, torch.Tensor, torch.Tensor]] = [tuple(h) for h in handles]
         arr = self._handle_array(handles)
         desc = LayerDesc(hidden, inter, n_experts, top_k)
         out = ctypes.c_void_p()
@@ -132,6 +133,7 @@ class Layer:
                                               _stream(stream)), "moe_layer_set_experts")
         for i, h in enumerate(handles):
             self._blobs[first + i] = (h[1], h[2])
+            self.handles[first + i] = tuple(h)
 
     def workspace_size(self, T: int) -> int:
         return int(self._lib.moe_workspace_size(self._h, int(T)))
@@ -241,7 +243,9 @@ class Layer:
                      out_dtype: torch.dtype = torch.float32,
                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         """One wave over the experts the current slot map sends to slots
-        (y = or y += the wave's output; accumulating needs an fp32 y)."""
+        (y = or y += the wave's output; accumulating needs an fp32 y and reuses
+        the routing the previous wave left in the workspace, so without an
+        explicit workspace the layer keeps one per token count for its waves)."""
         _require_cuda(x, "x", _BF16)
         _require_cuda(wr, "wr", _BF16)
         if bias is not None:
@@ -251,7 +255,14 @@ class Layer:
             y = torch.empty((T, self.hidden), dtype=out_dtype, device=x.device)
         _require_cuda(y, "y", (torch.float32, torch.bfloat16))
         yd = DTYPE_F32 if y.dtype == torch.float32 else DTYPE_BF16
-        ws = self.workspace(T, x.device) if workspace is None else workspace
+        if workspace is None:
+            cache = self.__dict__.setdefault("_wave_ws", {})
+            key = (T, str(x.device))
+            if key not in cache:
+                cache[key] = self.workspace(T, x.device)
+            ws = cache[key]
+        else:
+            ws = workspace
         check(self._lib.moe_layer_forward_wave(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), T,
                                                y.data_ptr(), yd, int(bool(accumulate)), ws.data_ptr(),
                                                ws.numel(), _stream(stream)), "moe_layer_forward_wave")

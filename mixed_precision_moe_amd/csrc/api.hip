@@ -467,13 +467,18 @@ T* at(void* ws, size_t off) {
 hipError_t enqueue_route(const Layer& L, WaveMap wave, Hotness hotness, const WsPlan& p, const GemmPlan& gp, const uint16_t* x,
                          const uint16_t* wr, const float* bias, int T, float* logits,
                          int32_t* ids, float* w, int32_t* offsets, int32_t* sorted, int32_t* pos,
-                         float* r13, void* ws, const Stages& st) {
+                         float* r13, void* ws, const Stages& st, bool reuse_topk = false) {
   st.rec(0);
-  hipError_t e = launch_router_logits(x, wr, bias, T, L.H, L.E, logits, r13, st.s);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!reuse_topk) {   // later waves of a layer call keep the first wave's routing
+    e = launch_router_logits(x, wr, bias, T, L.H, L.E, logits, r13, st.s);
+    if (e != hipSuccess) return e;
+  }
   st.rec(1);
-  e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
-  if (e != hipSuccess) return e;
+  if (!reuse_topk) {
+    e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
+    if (e != hipSuccess) return e;
+  }
   st.rec(2);
   return launch_permute(L.table, wave, hotness, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
                         at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
@@ -508,7 +513,7 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
                                at<int32_t>(ws, p.ids), at<float>(ws, p.weights),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
                                at<int32_t>(ws, p.pos), prefill ? nullptr : at<float>(ws, p.r13),
-                               ws, st);
+                               ws, st, wave.slot_map != nullptr && accumulate);
   if (e != hipSuccess) return check_hip(e, "route launch");
   st.rec(3);
   if (prefill) {

@@ -50,6 +50,12 @@ def test_layer_small_configs_full(cid):
     _run(Setup(cid))
 
 
+@pytest.mark.parametrize("T", [32, 512])
+def test_layer_olmoe_full(T):
+    """The OLMoE-shaped layer (H 2048, E 64, top-8, I 1024): decode and prefill."""
+    _run(Setup(6, T=T))
+
+
 @pytest.mark.parametrize("T", [1, 32, 256])
 def test_layer_qwen80b_sweep_full(T):
     _run(Setup(4, T=T), keep=False)

@@ -106,3 +106,29 @@ def test_sentinel_and_validation():
         layer.forward_wave(x, wr, b, y=torch.zeros((st.T, st.H), dtype=torch.bfloat16,
                                                    device=x.device), accumulate=True)
     assert ei.value.status == 1
+
+
+def test_sequential_per_expert_waves_olmoe():
+    """The OLMoE-shaped layer run one expert at a time (one wave per touched
+    expert, the routing kept from the first) equals the fused forward."""
+    import torch
+    st = Setup(6, T=32)
+    layer = st.gpu_layer()
+    x, wr, b = st.dev_inputs()
+    ol = st.oracle_layer()
+    y_ref, r = ol.forward(st.x, st.wr, st.bias)
+    layer.set_slots(0, layer.handles)
+    y = torch.zeros((st.T, st.H), dtype=torch.float32, device=x.device)
+    touched = sorted(set(int(e) for e in r["ids"].ravel()))
+    for i, e in enumerate(touched):
+        m = [-1] * st.E
+        m[e] = e
+        layer.set_slot_map(m)
+        layer.forward_wave(x, wr, b, y=y, accumulate=i > 0)
+    y_fused = layer.forward(x, wr, b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rms = float(np.sqrt(np.mean(y_ref.astype(np.float64) ** 2)))
+    gap = float(np.max(np.abs(y.cpu().numpy().astype(np.float64) - y_fused.cpu().numpy()))) / rms
+    err = rel_err(y.cpu().numpy(), y_ref)
+    log(f"olmoe sequential {len(touched)} waves: vs oracle {err:.2e}, vs fused {gap:.2e}")
+    assert err <= TOL and gap <= 1e-5
