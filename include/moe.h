@@ -261,8 +261,11 @@ int moe_layer_forward_wave(moe_layer_t layer, const uint16_t* x, const uint16_t*
 /* Optional timing hook: when events (hipEvent_t passed as void*) are set, each
  * forward records events[i] before stage i and events[n-1] after the last
  * stage, on the forward's stream.  Stages: 0 route logits, 1 top-k,
- * 2 grouping, 3 gate/up GEMM + SwiGLU, 4 down GEMM, 5 combine; n must be 7.
- * Pass n = 0 to turn it off.  The events are owned by the caller. */
+ * 2 grouping, 3 gate/up GEMM + SwiGLU, 4 down GEMM, 5 combine; n = 7.  With
+ * n = 9, events[7] and events[8] also receive the gate/up GEMM kernel's own
+ * start and end timestamps (hipExtLaunchKernelGGL), without the dispatch gaps
+ * a stage boundary includes.  Pass n = 0 to turn it off.  The events are owned
+ * by the caller. */
 int moe_layer_set_stage_events(moe_layer_t layer, void* const* events, int32_t n);
 
 /* Text of a status code (static storage). */

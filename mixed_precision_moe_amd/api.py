@@ -269,7 +269,8 @@ class Layer:
         return y
 
     def set_stage_events(self, events: Optional[Sequence["torch.cuda.Event"]]) -> None:
-        """Per-stage timing events (7 torch.cuda.Event with timing), or None."""
+        """Per-stage timing events (7 torch.cuda.Event with timing, or 9: the
+        last two get the gate/up GEMM kernel's own start and end), or None."""
         if not events:
             check(self._lib.moe_layer_set_stage_events(self._h, None, 0), "set_stage_events")
             self._events = None

@@ -417,7 +417,7 @@ int moe_layer_set_stage_events(moe_layer_t layer, void* const* events, int32_t n
   g_err[0] = 0;
   Layer* L = reinterpret_cast<Layer*>(layer);
   if (!L) return set_error(MOE_EINVAL, "null layer");
-  if (n != 0 && n != 7) return set_error(MOE_EINVAL, "need 0 or 7 events (got %d)", n);
+  if (n != 0 && n != 7 && n != 9) return set_error(MOE_EINVAL, "need 0, 7 or 9 events (got %d)", n);
   if (n && !events) return set_error(MOE_EINVAL, "null events");
   for (int i = 0; i < n; ++i) {
     if (!events[i]) return set_error(MOE_EINVAL, "null event %d", i);
@@ -454,8 +454,15 @@ struct Stages {
   hipStream_t s;
   bool on;
   void rec(int i) const {
-    if (on && L->n_stage_events == 7)
+    if (on && L->n_stage_events >= 7)
       (void)hipEventRecord(reinterpret_cast<hipEvent_t>(L->stage_events[i]), s);
+  }
+  // events 7 and 8: the gate/up GEMM kernel's own start and end
+  KernelTimer gate_up_timer() const {
+    if (on && L->n_stage_events == 9)
+      return KernelTimer{reinterpret_cast<hipEvent_t>(L->stage_events[7]),
+                         reinterpret_cast<hipEvent_t>(L->stage_events[8])};
+    return KernelTimer{nullptr, nullptr};
   }
 };
 
@@ -521,11 +528,11 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
     if (e == hipSuccess)
       e = launch_prefill(true, *L, T, at<uint16_t>(ws, p.x16), at<int32_t>(ws, p.sorted),
                          at<TileEntry>(ws, p.tiles13), at<int32_t>(ws, p.ntiles13), p.max_tiles13,
-                         at<uint16_t>(ws, p.act), nullptr, nullptr, s);
+                         at<uint16_t>(ws, p.act), nullptr, nullptr, s, st.gate_up_timer());
   } else {
     e = launch_gemm13(*L, gp, T, x, at<int32_t>(ws, p.sorted), at<TileEntry>(ws, p.tiles13),
                       at<int32_t>(ws, p.ntiles13), p.max_tiles13, at<float>(ws, p.r13),
-                      at<uint16_t>(ws, p.act), at<float>(ws, p.r2), s);
+                      at<uint16_t>(ws, p.act), at<float>(ws, p.r2), s, st.gate_up_timer());
   }
   if (e != hipSuccess) return check_hip(e, "gate/up GEMM launch");
   st.rec(4);

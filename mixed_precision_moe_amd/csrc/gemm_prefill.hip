@@ -26,6 +26,8 @@
 // LDS in fragment-major order (a 1 KB fragment holds one 16 x 32 operand with
 // lane l's 16 bytes at 16*l).  Each chunk: 2 x 8 x 4 v_mfma_f32_16x16x32_f16
 // per wave.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device_util.h"
@@ -556,7 +558,8 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream
 
 hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
-                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s) {
+                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s,
+                          KernelTimer kt) {
   PrefillArgs a{};
   a.tiles = tiles;
   a.ntiles = ntiles;
@@ -581,7 +584,10 @@ hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a
     attr[gate_up] = true;
   }
   const dim3 grid((unsigned)((a.N / PBN) * max_tiles));
-  if (gate_up)
+  if (gate_up && (kt.start || kt.stop))
+    hipExtLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPrefillThreads),
+                          (uint32_t)kPrefillLds, s, kt.start, kt.stop, 0, a);
+  else if (gate_up)
     hipLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPrefillThreads), kPrefillLds, s, a);
   else
     hipLaunchKernelGGL(gemm_prefill_kernel<false>, grid, dim3(kPrefillThreads), kPrefillLds, s, a);

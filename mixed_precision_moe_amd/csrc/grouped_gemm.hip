@@ -30,6 +30,8 @@
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout used here: lane l holds row
 // (A) / column (B) l%16 and the 8 k-values 8*(l/16) .. +7 of the 32-wide step;
 // the accumulator of lane l holds rows 4*(l/16) + i, column l%16.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device_util.h"
@@ -356,7 +358,7 @@ size_t decode_lds_bytes(int K) {
 }
 
 template <int NS, bool GATE_UP>
-hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s) {
+hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s, KernelTimer kt) {
   // waves per block: as many strips of one tile as divide N evenly, up to 8
   const int strips = a.N / 16;
   const int chunks = strips / NS;
@@ -372,7 +374,11 @@ hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s) {
       attr_set[W == 8] = true;
     }
     const int bpt = chunks / W;
-    hipLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), lds, s, a, bpt);
+    if (kt.start || kt.stop)
+      hipExtLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), (uint32_t)lds, s, kt.start,
+                            kt.stop, 0, a, bpt);
+    else
+      hipLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), lds, s, a, bpt);
     return hipGetLastError();
   };
   return run(std::integral_constant<int, 4>{});   // N is a multiple of 256: chunks % 4 == 0
@@ -429,7 +435,7 @@ GemmPlan plan_gemm(const Layer& L, int T) {
 hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16_t* x,
                          const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
                          int max_tiles, const float* r13, uint16_t* act, float* r2,
-                         hipStream_t s) {
+                         hipStream_t s, KernelTimer kt) {
   (void)T;
   GemmArgs a{};
   a.tiles = tiles;
@@ -444,7 +450,7 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.r2 = r2;
   a.I = L.I;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, true>(a, max_tiles, s);
+  return launch_decode<4, true>(a, max_tiles, s, kt);
 }
 
 hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
@@ -464,7 +470,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.topk_w = topk_w;
   a.rows = rows;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, false>(a, max_tiles, s);
+  return launch_decode<4, false>(a, max_tiles, s, KernelTimer{nullptr, nullptr});
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,

@@ -72,7 +72,7 @@ struct Layer {
   // routes to e (caller-owned device [E], or null)
   float* hot;
   float hot_decay;
-  void* stage_events[7];
+  void* stage_events[9];
   int32_t n_stage_events;
 };
 
@@ -82,6 +82,12 @@ struct Layer {
 struct WaveMap {
   const int32_t* slot_map;
   const DevHandle* slots;
+};
+
+// Optional start/stop events that receive one kernel's own timestamps
+// (hipExtLaunchKernelGGL); both null: an ordinary launch.
+struct KernelTimer {
+  hipEvent_t start, stop;
 };
 
 // Per-forward hotness update of the grouping kernels (hot null: none).
@@ -122,7 +128,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
 hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16_t* x,
                          const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
                          int max_tiles, const float* r13, uint16_t* act, float* r2,
-                         hipStream_t s);
+                         hipStream_t s, KernelTimer kt = KernelTimer{nullptr, nullptr});
 hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
                         const int32_t* sorted, const float* topk_w, const TileEntry* tiles,
                         const int32_t* ntiles, int max_tiles, const float* r2, float* rows,
@@ -131,7 +137,7 @@ size_t prefill_lds_bytes();
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
-                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s);
+                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s, KernelTimer kt = KernelTimer{nullptr, nullptr});
 // y[t] (=|+=) sum over the token's routes in ascending expert order; with a
 // slot map, routes whose expert maps to the sentinel are skipped.
 hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
