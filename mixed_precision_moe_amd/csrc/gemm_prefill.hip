@@ -6,7 +6,8 @@
 // into arithmetic.  Weights are dequantized in registers, never materialized
 // as a full fp16 matrix (§3.1, §3.3); as in the MARLIN kernel the pages use,
 // the dequantized weight q*s is rounded once to fp16 (relative error at most
-// 2^-12) and the product runs on fp16 MFMA with fp32 accumulation.
+// 2^-11, fp16's unit roundoff, for scales in fp16's normal range) and the
+// product runs on fp16 MFMA with fp32 accumulation.
 // Activations enter as fp16 re-encodings of their bf16 values (exact for
 // magnitudes in [2^-14, 65504]; larger magnitudes saturate to +-65504).
 //
