@@ -73,6 +73,14 @@ typedef enum moe_tier {
   MOE_TIER_INT4 = 2   /* symmetric int4, one fp16 scale per (row, 128 inputs)  */
 } moe_tier;
 
+/* How a routing call without logits output computes its top k (the result
+ * is the same bit for bit; see moe_route). */
+typedef enum moe_router_mode {
+  MOE_ROUTER_AUTO = 0,       /* MFMA router when T*E*H is large (default)      */
+  MOE_ROUTER_CANONICAL = 1,  /* always the fixed-order fp32 logits kernel      */
+  MOE_ROUTER_MFMA = 2        /* MFMA router whenever the call allows it        */
+} moe_router_mode;
+
 /* Row order of a packed matrix. */
 typedef enum moe_layout {
   MOE_LAYOUT_PLAIN = 0,   /* down projection W_d [H, I]                        */
@@ -199,6 +207,12 @@ int moe_plan_tiers(const float* hot, int32_t n_experts, const size_t* bytes_per_
                    size_t budget_bytes, int32_t hi_tier, int32_t lo_tier, int32_t* tiers_out,
                    int32_t* n_hi_out);
 
+/* Router choice of later route and forward calls (moe_router_mode).  The
+ * MFMA router needs workspace of its own: size the workspace after setting
+ * the mode.  A decode-sized forward (a few routes per expert) always takes
+ * the fixed-order kernel, which also produces the GEMM's group sums. */
+int moe_layer_set_router_mode(moe_layer_t layer, int32_t mode);
+
 /* Free the layer's device state.  The caller must have synchronized every
  * stream that has work using the layer. */
 int moe_layer_destroy(moe_layer_t layer);
@@ -221,6 +235,11 @@ size_t moe_workspace_size(moe_layer_t layer, int32_t T);
  *                  group in increasing token order.
  *   route_pos      [T*k] int32: position of route r in sorted_routes.
  *   ws: device workspace of ws_bytes >= moe_workspace_size(layer, T).
+ * With logits NULL the call may take the MFMA router (moe_layer_set_router_mode;
+ * by default when T >= 256, E >= 32 and T*E*H >= 2^29): approximate logits on
+ * bf16 MFMA and an error bound against this fixed order leave a few candidate
+ * experts per token, whose logits are then summed in the fixed order; the
+ * results are the same bit for bit.
  * T may be 0 (then only expert_offsets is written, all zero). */
 int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
               const float* bias, int32_t T, int32_t* topk_ids, float* topk_w,

@@ -11,6 +11,9 @@ from ._lib import LIB_PATH, MoeError, load  # noqa: F401
 from .api import (  # noqa: F401
     LAYOUT_GATE_UP,
     LAYOUT_PLAIN,
+    ROUTER_AUTO,
+    ROUTER_CANONICAL,
+    ROUTER_MFMA,
     TIER_BF16,
     TIER_INT4,
     TIER_INT8,

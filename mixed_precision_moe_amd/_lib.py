@@ -18,6 +18,7 @@ MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_ERANGE, MOE_ENOSPC, MOE_EHIP = range(6)
 TIER_BF16, TIER_INT8, TIER_INT4 = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_GATE_UP = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
+ROUTER_AUTO, ROUTER_CANONICAL, ROUTER_MFMA = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = (
@@ -25,7 +26,7 @@ EXPORTS = (
     "moe_layer_set_experts", "moe_layer_set_slots", "moe_layer_set_slot_map",
     "moe_layer_set_hotness", "moe_plan_tiers", "moe_layer_destroy", "moe_workspace_size",
     "moe_route", "moe_layer_forward", "moe_layer_forward_wave", "moe_layer_set_stage_events",
-    "moe_strerror", "moe_last_error", "moe_abi_version",
+    "moe_layer_set_router_mode", "moe_strerror", "moe_last_error", "moe_abi_version",
 )
 
 
@@ -78,6 +79,7 @@ def load() -> ctypes.CDLL:
         "moe_layer_forward_wave": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, ctypes.c_int, ctypes.c_int,
                                                   vp, sz, vp]),
         "moe_layer_set_stage_events": (ctypes.c_int, [vp, ctypes.POINTER(vp), i32]),
+        "moe_layer_set_router_mode": (ctypes.c_int, [vp, i32]),
         "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int, []),

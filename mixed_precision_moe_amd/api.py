@@ -13,11 +13,13 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUT_GATE_UP, LAYOUT_PLAIN, TIER_BF16, TIER_INT4,
-                   TIER_INT8, ExpertHandle, LayerDesc, MoeError, check)
+from ._lib import (DTYPE_BF16, DTYPE_F32, LAYOUT_GATE_UP, LAYOUT_PLAIN, ROUTER_AUTO,
+                   ROUTER_CANONICAL, ROUTER_MFMA, TIER_BF16, TIER_INT4, TIER_INT8, ExpertHandle,
+                   LayerDesc, MoeError, check)
 
 __all__ = [
     "TIER_BF16", "TIER_INT8", "TIER_INT4", "LAYOUT_PLAIN", "LAYOUT_GATE_UP", "MoeError",
+    "ROUTER_AUTO", "ROUTER_CANONICAL", "ROUTER_MFMA",
     "packed_size", "quantize_pack", "pack_expert", "Layer",
 ]
 
@@ -149,7 +151,10 @@ class Layer:
         return ws
 
     def route(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+              workspace: Optional[torch.Tensor] = None, stream=None,
+              want_logits: bool = True) -> Dict[str, torch.Tensor]:
+        """Routing only.  want_logits=False lets many-token calls use the
+        certified MFMA router (same ids, weights and permutation)."""
         _require_cuda(x, "x", _BF16)
         _require_cuda(wr, "wr", _BF16)
         if bias is not None:
@@ -160,7 +165,7 @@ class Layer:
         out = dict(
             ids=torch.empty((T, k), dtype=torch.int32, device=dev),
             weights=torch.empty((T, k), dtype=torch.float32, device=dev),
-            logits=torch.empty((T, E), dtype=torch.float32, device=dev),
+            logits=torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None,
             offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
             sorted_routes=torch.empty(T * k, dtype=torch.int32, device=dev),
             route_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
@@ -168,9 +173,11 @@ class Layer:
         ws = self.workspace(T, dev) if workspace is None else workspace
         check(self._lib.moe_route(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), T,
                                   out["ids"].data_ptr(), out["weights"].data_ptr(),
-                                  out["logits"].data_ptr(), out["offsets"].data_ptr(),
+                                  _ptr(out["logits"]), out["offsets"].data_ptr(),
                                   out["sorted_routes"].data_ptr(), out["route_pos"].data_ptr(),
                                   ws.data_ptr(), ws.numel(), _stream(stream)), "moe_route")
+        if not want_logits:
+            del out["logits"]
         return out
 
     def forward(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor] = None,
@@ -281,6 +288,14 @@ class Layer:
         arr = (ctypes.c_void_p * len(events))(*[ev.cuda_event for ev in events])
         check(self._lib.moe_layer_set_stage_events(self._h, arr, len(events)), "set_stage_events")
         self._events = list(events)
+
+    def set_router_mode(self, mode: int) -> None:
+        """ROUTER_AUTO, ROUTER_CANONICAL or ROUTER_MFMA for later calls (same
+        routing bit for bit; the workspace size may change, so the cached
+        workspaces are dropped)."""
+        check(self._lib.moe_layer_set_router_mode(self._h, int(mode)), "set_router_mode")
+        self._ws.clear()
+        self.__dict__.pop("_wave_ws", None)
 
     def close(self) -> None:
         if getattr(self, "_h", None):

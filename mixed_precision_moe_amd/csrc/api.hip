@@ -47,7 +47,11 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
     o = round_up(o + bytes, kBlobAlign);
     return at;
   };
-  w.logits = take(sizeof(float) * T * (size_t)L.E);
+  // the MFMA router (any call of this size may take it) keeps S partial
+  // logit rows per token here
+  const bool cert = use_certified_router(L.router_mode, T, L.E, L.H);
+  const size_t S = cert ? (size_t)router_split(T, L.E, L.H) : 1;
+  w.logits = take(sizeof(float) * T * (size_t)L.E * S);
   w.ids = take(sizeof(int32_t) * R);
   w.weights = take(sizeof(float) * R);
   w.offsets = take(sizeof(int32_t) * (L.E + 1));
@@ -55,6 +59,8 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
   w.pos = take(sizeof(int32_t) * R);
   w.rank = take(sizeof(int32_t) * R);
   w.chunk_counts = take(sizeof(int32_t) * (size_t)((T + kPermChunk - 1) / kPermChunk) * L.E);
+  w.xn2 = take(sizeof(float) * (size_t)T * S);
+  w.wn2 = take(sizeof(float) * (size_t)L.E * S);
   w.tiles13 = take(sizeof(TileEntry) * (size_t)(w.max_tiles13 > 0 ? w.max_tiles13 : 1));
   w.ntiles13 = take(sizeof(int32_t));
   w.tiles2 = take(sizeof(TileEntry) * (size_t)(w.max_tiles2 > 0 ? w.max_tiles2 : 1));
@@ -267,6 +273,7 @@ int moe_layer_create(const moe_layer_desc* d, const moe_expert_handle* table, vo
   L->E = d->n_experts;
   L->k = d->top_k;
   L->n_stage_events = 0;
+  L->router_mode = MOE_ROUTER_AUTO;
   L->table = nullptr;
   L->hot = nullptr;
   L->hot_decay = 1.0f;
@@ -427,6 +434,16 @@ int moe_layer_set_stage_events(moe_layer_t layer, void* const* events, int32_t n
   return MOE_OK;
 }
 
+int moe_layer_set_router_mode(moe_layer_t layer, int32_t mode) {
+  g_err[0] = 0;
+  Layer* L = reinterpret_cast<Layer*>(layer);
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  if (mode != MOE_ROUTER_AUTO && mode != MOE_ROUTER_CANONICAL && mode != MOE_ROUTER_MFMA)
+    return set_error(MOE_EINVAL, "bad router mode %d", mode);
+  L->router_mode = mode;
+  return MOE_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -477,14 +494,25 @@ hipError_t enqueue_route(const Layer& L, WaveMap wave, Hotness hotness, const Ws
                          float* r13, void* ws, const Stages& st, bool reuse_topk = false) {
   st.rec(0);
   hipError_t e = hipSuccess;
-  if (!reuse_topk) {   // later waves of a layer call keep the first wave's routing
-    e = launch_router_logits(x, wr, bias, T, L.H, L.E, logits, r13, st.s);
+  // Many tokens, logits not wanted (null): logits on MFMA, the top k taken
+  // from the candidates the error bound leaves, recomputed in the canonical
+  // order (the same routing bit for bit, see router_certified.hip).
+  if (!reuse_topk && !logits && !r13 && use_certified_router(L.router_mode, T, L.E, L.H)) {
+    e = launch_router_certified(x, wr, bias, T, L.H, L.E, L.k, at<float>(ws, p.logits),
+                                at<float>(ws, p.xn2), at<float>(ws, p.wn2), ids, w, st.s);
     if (e != hipSuccess) return e;
-  }
-  st.rec(1);
-  if (!reuse_topk) {
-    e = launch_topk(logits, T, L.E, L.k, ids, w, st.s);
-    if (e != hipSuccess) return e;
+    st.rec(1);
+  } else {
+    float* z = logits ? logits : at<float>(ws, p.logits);
+    if (!reuse_topk) {   // later waves of a layer call keep the first wave's routing
+      e = launch_router_logits(x, wr, bias, T, L.H, L.E, z, r13, st.s);
+      if (e != hipSuccess) return e;
+    }
+    st.rec(1);
+    if (!reuse_topk) {
+      e = launch_topk(z, T, L.E, L.k, ids, w, st.s);
+      if (e != hipSuccess) return e;
+    }
   }
   st.rec(2);
   return launch_permute(L.table, wave, hotness, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
@@ -516,7 +544,7 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
   // the hotness trace counts each layer call once: a plain forward, or the
   // first wave of a layer call (the one that does not accumulate)
   const Hotness hotness{accumulate ? nullptr : L->hot, L->hot_decay};
-  hipError_t e = enqueue_route(*L, wave, hotness, p, gp, x, wr, bias, T, at<float>(ws, p.logits),
+  hipError_t e = enqueue_route(*L, wave, hotness, p, gp, x, wr, bias, T, nullptr,
                                at<int32_t>(ws, p.ids), at<float>(ws, p.weights),
                                at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.sorted),
                                at<int32_t>(ws, p.pos), prefill ? nullptr : at<float>(ws, p.r13),
@@ -577,8 +605,7 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const fl
                      "hipMemsetAsync(offsets)");
   const Stages st{L, s, false};
   const hipError_t e = enqueue_route(*L, WaveMap{nullptr, nullptr}, Hotness{nullptr, 1.0f}, p, gp,
-                                     x, wr, bias, T,
-                                     logits ? logits : at<float>(ws, p.logits), topk_ids, topk_w,
+                                     x, wr, bias, T, logits, topk_ids, topk_w,
                                      expert_offsets, sorted_routes, route_pos, nullptr, ws, st);
   return check_hip(e, "route launch");
 }

@@ -15,6 +15,30 @@ constexpr int kMaxTopK = 16;
 constexpr int kBlobAlign = 256;
 constexpr int kPermSmallT = 1024;  // largest T grouped by the single-workgroup kernel
 constexpr int kPermChunk = 256;    // tokens per block of the multi-block grouping
+constexpr int kCertifiedMinT = 256;   // fewest tokens routed by the MFMA router
+constexpr int kCertifiedMinE = 32;    // fewest experts for it
+constexpr double kCertifiedMinFma = 536870912.0;  // fewest T*E*H for it (2^29)
+constexpr int kRouterMaxSplit = 8;    // most K splits across blocks of the MFMA router
+
+// Whether a routing call that wants no logits takes the MFMA router
+// (router_certified.hip): in auto mode, calls large enough for it to beat the
+// canonical fp32 kernel (which costs T*E*H FMAs).
+inline bool use_certified_router(int mode, int T, int E, int H) {
+  if (mode == MOE_ROUTER_CANONICAL) return false;
+  if (mode == MOE_ROUTER_MFMA) return T > 0;
+  return T >= kCertifiedMinT && E >= kCertifiedMinE && (double)T * E * H >= kCertifiedMinFma;
+}
+
+// K splits across blocks of the MFMA router logits: a power of two dividing
+// H / 256 (so each wave's K slice is a multiple of 64), raised until the grid
+// has about four blocks per CU.
+inline int router_split(int T, int E, int H) {
+  const long blocks = (long)((T + 31) / 32) * ((E + 63) / 64);
+  const int m = H / 256;
+  int S = 1;
+  while (2 * S <= kRouterMaxSplit && m % (2 * S) == 0 && blocks * S < 1024) S *= 2;
+  return S;
+}
 
 // Device copy of one expert handle (same field order as moe_expert_handle).
 struct DevHandle {
@@ -53,7 +77,7 @@ struct GemmPlan {
 // Byte offsets of the workspace regions for T tokens.
 struct WsPlan {
   size_t logits, ids, weights, offsets, sorted, pos, tiles13, ntiles13, tiles2, ntiles2;
-  size_t rank, chunk_counts;
+  size_t rank, chunk_counts, xn2, wn2;
   size_t r13, act, r2, rows, x16;
   size_t total;
   int max_tiles13, max_tiles2;
@@ -74,6 +98,7 @@ struct Layer {
   float hot_decay;
   void* stage_events[9];
   int32_t n_stage_events;
+  int32_t router_mode;   // moe_router_mode
 };
 
 // Wave mode of one forward: expert e runs from slots[slot_map[e]] when that
@@ -113,8 +138,14 @@ hipError_t launch_quantize_pack(int tier, int layout, const uint16_t* w, int64_t
 hipError_t launch_set_slot_map(int32_t* map, const int32_t* host_map, int E, hipStream_t s);
 hipError_t launch_set_handles(DevHandle* table, int first, int count,
                               const moe_expert_handle* h, hipStream_t s);
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
-                                int T, int H, int E, float* logits, float* r13, hipStream_t s);
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                                int H, int E, float* logits, float* r13, hipStream_t s);
+// Routing for many tokens with the logits on MFMA, certified against the
+// canonical order: writes ids and weights as launch_topk does.  Workspace,
+// with S = router_split(T, E, H): v [S, T, E], xn2 [S, T], wn2 [S, E].
+hipError_t launch_router_certified(const uint16_t* x, const uint16_t* wr, const float* bias, int T,
+                                   int H, int E, int k, float* v, float* xn2, float* wn2,
+                                   int32_t* ids, float* w, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t s);
 // Grouping: one workgroup for T <= kPermSmallT, else a rank pass and a

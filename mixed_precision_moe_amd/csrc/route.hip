@@ -14,6 +14,7 @@
 // fold is a shuffle tree.
 #include "device_util.h"
 #include "moe_internal.h"
+#include "topk_select.h"
 
 namespace moe {
 namespace {
@@ -120,19 +121,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-// better(a, b): larger logit, or equal logit and lower expert id.
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-  return va > vb || (va == vb && ea < eb);
-}
-
-extern "C" __device__ float __ockl_wfred_max_f32(float);
-extern "C" __device__ int __ockl_wfred_min_i32(int);
-
-// One wave per token: select the k largest logits (ties -> lower id), softmax
-// over them, store ids ascending with their weights.  Each round takes the
-// lane-local best of the not-yet-taken experts (lane l holds experts
-// l, l+64, ...), a wave max of the logit (DPP reduction), and, only if several
-// lanes hold that maximum, a wave min of their expert ids.
+// One wave per token: the k largest logits (ties -> lower id) and their
+// softmax weights, stored with ids ascending (topk_select.h).  Lane l holds
+// experts l, l+64, ...
 constexpr int kMaxPerLane = kMaxExperts / 64;
 
 // PER (a power of two, PER * 64 >= E) is the compile-time bound of the
@@ -146,64 +137,16 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logi
   if (t >= T) return;
   const float* z = logits + (size_t)t * E;
   float v[PER];
+  int id[PER];
   const int per = (E + 63) / 64;
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
     const int e = lane + 64 * m;
-    v[m] = (m < per && e < E) ? z[e] : -INFINITY;
+    const bool ok = m < per && e < E;
+    v[m] = ok ? z[e] : -INFINITY;
+    id[m] = ok ? e : kNoExpert;
   }
-  uint32_t taken = 0;
-  int sel_e[kMaxTopK];
-  float sel_z[kMaxTopK];
-#pragma unroll
-  for (int jj = 0; jj < kMaxTopK; ++jj) {
-    if (jj >= k) break;
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int e = lane + 64 * m;
-      if (m < per && e < E && !((taken >> m) & 1u) && better(v[m], e, bv, be)) {
-        bv = v[m];
-        be = e;
-      }
-    }
-    const float wmax = __ockl_wfred_max_f32(bv);
-    const bool cand = bv == wmax && be < E;
-    const uint64_t mask = __ballot(cand);
-    int we;
-    if (__popcll(mask) == 1)
-      we = __builtin_amdgcn_readlane(be, __ffsll((unsigned long long)mask) - 1);
-    else
-      we = __ockl_wfred_min_i32(cand ? be : 0x7fffffff);
-    if (we >= E || we < 0) we = jj;   // only reachable with NaN logits (out of domain)
-    if ((we & 63) == lane) taken |= 1u << (we >> 6);
-    sel_e[jj] = we;
-    sel_z[jj] = wmax;
-  }
-  // softmax over the selected logits (the first selected one is the largest)
-  if (lane < k) {
-    int my_e = 0;
-    float my_z = 0.0f, den = 0.0f;
-    const float zmax = sel_z[0];
-#pragma unroll
-    for (int jj = 0; jj < kMaxTopK; ++jj) {
-      if (jj >= k) break;
-      den += expf(sel_z[jj] - zmax);
-      if (jj == lane) {
-        my_e = sel_e[jj];
-        my_z = sel_z[jj];
-      }
-    }
-    int rank = 0;
-#pragma unroll
-    for (int jj = 0; jj < kMaxTopK; ++jj) {
-      if (jj >= k) break;
-      rank += sel_e[jj] < my_e;
-    }
-    ids[(size_t)t * k + rank] = my_e;
-    weights[(size_t)t * k + rank] = expf(my_z - zmax) / den;
-  }
+  topk_select_softmax<PER>(v, id, k, ids + (size_t)t * k, weights + (size_t)t * k);
 }
 
 // Exclusive prefix sum over the 1024 threads of a block; also returns the total.

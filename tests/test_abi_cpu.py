@@ -114,6 +114,7 @@ def test_null_layer_calls():
     assert lib.moe_route(None, FAKE, FAKE, None, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                          1 << 20, None) == _lib.MOE_EINVAL
     assert lib.moe_layer_set_stage_events(None, None, 0) == _lib.MOE_EINVAL
+    assert lib.moe_layer_set_router_mode(None, _lib.ROUTER_AUTO) == _lib.MOE_EINVAL
     assert lib.moe_layer_set_slots(None, 0, 1, _handles(1), None) == _lib.MOE_EINVAL
     assert lib.moe_layer_set_slot_map(None, (ctypes.c_int32 * 4)(-1, -1, -1, -1), None) == _lib.MOE_EINVAL
     assert lib.moe_layer_forward_wave(None, FAKE, FAKE, None, 4, FAKE, 1, 1, FAKE, 1 << 20,

@@ -65,3 +65,108 @@ def test_route_large_bias_forces_experts():
     b[[3, 77, 100, 101, 5, 9, 64, 127]] = 1000.0
     st.bias = b
     _check_route(st)
+
+
+def _route_np(layer, st, want_logits):
+    import torch
+    x, wr, b = st.dev_inputs()
+    got = {k: v.cpu().numpy() for k, v in layer.route(x, wr, b, want_logits=want_logits).items()}
+    torch.cuda.synchronize()
+    return got
+
+
+def _mfma_layer(st):
+    from mixed_precision_moe_amd import ROUTER_MFMA
+    layer = st.gpu_layer(experts=[0])
+    layer.set_router_mode(ROUTER_MFMA)
+    return layer
+
+
+@pytest.mark.parametrize("cid,T", [(3, 512), (4, 4096), (4, 1025), (6, 512), (4, 256),
+                                   (1, 37), (2, 1), (5, 300), (4, 33)])
+def test_certified_router_matches_canonical(cid, T):
+    """Without logits output, the MFMA router (approximate logits, error-bound
+    candidates, canonical recompute) gives the canonical routing bit for bit
+    (ids, weights, offsets, permutation), and the oracle's: ragged token
+    tiles, one token, E below one 64-expert tile (E = 8, 32)."""
+    st = Setup(cid, T=T)
+    layer = _mfma_layer(st)
+    log(f"MFMA route cfg{cid} T={T} E={st.E} k={st.k}")
+    fast = _route_np(layer, st, False)
+    canon = _route_np(layer, st, True)
+    for key in ("ids", "offsets", "sorted_routes", "route_pos"):
+        assert np.array_equal(fast[key], canon[key]), key
+    assert np.array_equal(fast["weights"].view(np.uint32), canon["weights"].view(np.uint32))
+    ref = oracle.route(st.x, st.wr, st.bias, st.k)
+    assert np.array_equal(fast["ids"], ref["ids"])
+    assert np.max(np.abs(fast["weights"] - ref["weights"])) <= 1e-6
+
+
+def test_certified_router_exact_ties_among_candidates():
+    """The router rows (and biases) come in groups of four exact copies, so the
+    top-k boundary of every token (k = 10) cuts through a group of equal
+    logits: the whole group is among the candidates and the canonical tie
+    rule (lower id first) decides inside the MFMA router's selection."""
+    st = Setup(4, T=512)
+    B = st.E // 4
+    wr = st.wr.copy()
+    for g in range(1, 4):
+        wr[g * B:(g + 1) * B] = wr[:B]
+    st.wr = wr
+    if st.bias is not None:
+        b = st.bias.copy()
+        for g in range(1, 4):
+            b[g * B:(g + 1) * B] = b[:B]
+        st.bias = b
+    assert st.k % 4 != 0
+    layer = _mfma_layer(st)
+    fast = _route_np(layer, st, False)
+    canon = _route_np(layer, st, True)
+    for key in ("ids", "offsets", "sorted_routes", "route_pos"):
+        assert np.array_equal(fast[key], canon[key]), key
+    assert np.array_equal(fast["weights"].view(np.uint32), canon["weights"].view(np.uint32))
+    ref = oracle.route(st.x, st.wr, st.bias, st.k)
+    assert np.array_equal(fast["ids"], ref["ids"])
+    # whole groups first, then the lowest copies of the cut group
+    q, r = divmod(st.k, 4)
+    want = np.array([q + (g < r) for g in range(4)])
+    counts = np.stack([np.sum(fast["ids"] // B == g, axis=1) for g in range(4)], axis=1)
+    assert np.all(counts == want)
+
+
+def test_certified_router_full_ties():
+    """Every other token is zero and there is no bias: all of its logits are
+    exactly 0, every expert stays a candidate, and the canonical recompute of
+    all of them routes the token to the k lowest ids with equal weights; the
+    other tokens have a few candidates each, in the same call."""
+    st = Setup(4, T=384, bias=None)
+    x = st.x.copy()
+    x[::2] = 0
+    st.x = x
+    layer = _mfma_layer(st)
+    fast = _route_np(layer, st, False)
+    canon = _route_np(layer, st, True)
+    for key in ("ids", "offsets", "sorted_routes", "route_pos"):
+        assert np.array_equal(fast[key], canon[key]), key
+    assert np.array_equal(fast["weights"].view(np.uint32), canon["weights"].view(np.uint32))
+    ref = oracle.route(st.x, st.wr, st.bias, st.k)
+    assert np.array_equal(fast["ids"], ref["ids"])
+    assert np.max(np.abs(fast["weights"] - ref["weights"])) <= 1e-6
+    assert np.all(fast["ids"][::2] == np.arange(st.k)[None, :])
+    assert np.max(np.abs(fast["weights"][::2] - 1.0 / st.k)) <= 1e-6
+
+
+def test_router_mode_workspace_and_errors():
+    """The MFMA router needs its partial logits in the workspace: the size
+    follows the mode, and a bad mode is refused."""
+    from mixed_precision_moe_amd import ROUTER_AUTO, ROUTER_CANONICAL, ROUTER_MFMA, MoeError
+    st = Setup(3, T=64)
+    layer = st.gpu_layer(experts=[0])
+    layer.set_router_mode(ROUTER_CANONICAL)
+    small = layer.workspace_size(512)
+    layer.set_router_mode(ROUTER_MFMA)
+    big = layer.workspace_size(512)
+    assert big > small
+    layer.set_router_mode(ROUTER_AUTO)
+    with pytest.raises(MoeError):
+        layer.set_router_mode(7)
