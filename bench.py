@@ -209,6 +209,35 @@ def compare_sequential(layer, x, wr, bias, ids, T, H, dev, fused_fwd, reps):
                                "down GEMM, accumulate"}
 
 
+def dense_gemm_reference(M, K, N, dev, reps=20):
+    """Context for an MFMA-bound gate/up kernel: the vendor library's dense
+    GEMM (torch.matmul, i.e. hipBLASLt) on the same total shape [M, K] x
+    [K, N], in fp16 and bf16, timed with events on this GPU.  It has no
+    grouping, gathering, dequantization or epilogue, so it bounds what a
+    16-bit MFMA GEMM of this size reaches here at this GPU's sustained clock."""
+    import torch
+    res = {"library": "torch.matmul (hipBLASLt)", "shape_mkn": [M, K, N]}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for name, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        a = torch.randn(M, K, device=dev, dtype=dt, generator=g)
+        b = torch.randn(K, N, device=dev, dtype=dt, generator=g)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            c = a @ b
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / reps * 1000.0
+        res[f"{name}_us"] = round(us, 1)
+        res[f"{name}_tflops"] = round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1)
+        del a, b, c
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +253,9 @@ def main():
     ap.add_argument("--compare-sequential", action="store_true",
                     help="also time the same layer run one expert at a time (per-expert waves "
                          "through the slot map) against the fused grouped forward")
+    ap.add_argument("--no-dense-reference", action="store_true",
+                    help="skip timing the vendor dense GEMM of the same total shape beside an "
+                         "MFMA-bound gate/up kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run plain device copies of this many MiB (for scaling HBM "
                          "counters) and exit")
@@ -351,6 +383,12 @@ def main():
                       "forward's stream, averaged over the host-launched timed region")
     roof["algorithmic_per_launch"] = alg["flops13"] if prefill else alg["bytes13"]
     roof["traffic"] = stored_traffic(workload_key, "prefill" if prefill else "decode")
+    if prefill and not args.no_dense_reference:
+        ref = dense_gemm_reference(T * cfg.top_k, cfg.hidden, 2 * cfg.inter, dev)
+        ref["kernel_vs_f16"] = round(achieved / ref["f16_tflops"], 3)
+        roof["dense_gemm_reference"] = ref
+        log(f"[bench] dense f16 GEMM of the same total shape: {ref['f16_tflops']} TFLOP/s "
+            f"(bf16 {ref['bf16_tflops']}); the gate/up kernel reaches {ref['kernel_vs_f16']} of it")
 
     layer_roof_s = max(alg["bytes_layer"] / (HBM_PEAK_GBS * 1e9),
                        alg["flops_layer"] / (BF16_PEAK_TFLOPS * 1e12))
