@@ -276,8 +276,11 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     if (g0 + D + d < G) consume(g0 + D + d, d);
 }
 
+// Occupancy: three waves per SIMD for gate/up (K = H, long weight streams);
+// four for down, whose short K (I) makes more, shorter waves, all of which
+// then fit in one round at the decode workloads.
 template <int NS, int WAVES, bool GATE_UP>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 3 : 4, GATE_UP ? 3 : 4)))
 void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
   static_assert(NS == 1 || NS == 2 || NS == 4, "a wave's strips lie in one quad");
@@ -387,8 +390,10 @@ hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s, Kernel
 
 // Sum of a token's k weighted rows in ascending expert order, fp32.  With a
 // slot map (wave mode) routes of experts mapped to the sentinel are skipped,
-// and with ACC the sum is added to y (fp32 only).
-template <bool BF16_OUT, bool ACC>
+// and with ACC the sum is added to y (fp32 only).  KMAX >= k is the
+// compile-time bound of the route loops: every row load is issued before the
+// first add (loads past k repeat route k-1's row and are not added).
+template <bool BF16_OUT, bool ACC, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
                                                       const int32_t* __restrict__ pos,
                                                       const int32_t* __restrict__ ids,
@@ -396,15 +401,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int H, int k, void* __restrict__ y) {
   const int t = blockIdx.y;
   const int h4 = (blockIdx.x * 256 + threadIdx.x) * 4;
-  if (h4 >= H) return;
+  // lane j of each wave loads route j's position (one vector load), then
+  // every lane takes all of them with readlane (k is block-uniform)
+  const int lane = threadIdx.x & 63;
+  const int jl = min(lane, k - 1);
+  const int my_pos = pos[t * k + jl];
+  uint64_t keep = ~0ull;
+  if (slot_map) keep = __ballot(slot_map[ids[t * k + jl]] >= 0);   // wave mode
+  if (h4 >= H) return;   // after the wave-wide loads above
+  float4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    v[j] = *reinterpret_cast<const float4*>(rows + (size_t)__builtin_amdgcn_readlane(my_pos, j) * H + h4);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    if (slot_map && slot_map[ids[t * k + j]] < 0) continue;
-    const float4 v = *reinterpret_cast<const float4*>(rows + (size_t)pos[t * k + j] * H + h4);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const bool use = j < k && ((keep >> j) & 1ull);
+    s.x = use ? s.x + v[j].x : s.x;
+    s.y = use ? s.y + v[j].y : s.y;
+    s.z = use ? s.z + v[j].z : s.z;
+    s.w = use ? s.w + v[j].w : s.w;
   }
   if constexpr (BF16_OUT) {
     const uint32_t lo = f32_to_bf16_rne(s.x) | (f32_to_bf16_rne(s.y) << 16);
@@ -477,16 +493,24 @@ hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* 
                           const int32_t* slot_map, int T, int H, int k, void* y, int y_dtype,
                           bool accumulate, hipStream_t s) {
   const dim3 grid((H / 4 + 255) / 256, T);
-  if (y_dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL((combine_kernel<true, false>), grid, dim3(256), 0, s, rows, pos, ids, slot_map,
-                       T, H, k, y);
-  else if (accumulate)
-    hipLaunchKernelGGL((combine_kernel<false, true>), grid, dim3(256), 0, s, rows, pos, ids, slot_map,
-                       T, H, k, y);
-  else
-    hipLaunchKernelGGL((combine_kernel<false, false>), grid, dim3(256), 0, s, rows, pos, ids,
-                       slot_map, T, H, k, y);
-  return hipGetLastError();
+  auto run = [&](auto kmax) {
+    constexpr int KM = decltype(kmax)::value;
+    if (y_dtype == MOE_DTYPE_BF16)
+      hipLaunchKernelGGL((combine_kernel<true, false, KM>), grid, dim3(256), 0, s, rows, pos, ids,
+                         slot_map, T, H, k, y);
+    else if (accumulate)
+      hipLaunchKernelGGL((combine_kernel<false, true, KM>), grid, dim3(256), 0, s, rows, pos, ids,
+                         slot_map, T, H, k, y);
+    else
+      hipLaunchKernelGGL((combine_kernel<false, false, KM>), grid, dim3(256), 0, s, rows, pos, ids,
+                         slot_map, T, H, k, y);
+    return hipGetLastError();
+  };
+  static_assert(kMaxTopK <= 16, "combine buckets");
+  if (k <= 2) return run(std::integral_constant<int, 2>{});
+  if (k <= 4) return run(std::integral_constant<int, 4>{});
+  if (k <= 8) return run(std::integral_constant<int, 8>{});
+  return run(std::integral_constant<int, 16>{});
 }
 
 }  // namespace moe

@@ -177,8 +177,24 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
 // with c_e routes gets ceil(c_e / bm) tiles of each grouped GEMM, each entry
 // carrying the expert's tier and packed weights from the handle table (or, in
 // wave mode, from its resident slot).
-__device__ __forceinline__ void write_tile_tables(const DevHandle* table, WaveMap wave,
-                                                  Hotness hotness, const int* off, int E,
+// The handle of expert e = thread e (and whether wave mode gives it a slot):
+// independent of the grouping, so callers load it first and its latency
+// overlaps the counting.
+struct TileSource {
+  DevHandle h;
+  bool active;
+};
+__device__ __forceinline__ TileSource tile_source(const DevHandle* table, WaveMap wave, int E) {
+  const int e = min((int)threadIdx.x, E - 1);
+  // wave mode: only experts mapped to a resident slot get tiles, with the
+  // slot's weights (ExactMoE 3.4: the other experts map to the sentinel)
+  const int slot = wave.slot_map ? wave.slot_map[e] : 0;
+  const bool active = !wave.slot_map || (slot >= 0 && slot < E);
+  return TileSource{wave.slot_map ? wave.slots[active ? slot : 0] : table[e], active};
+}
+
+__device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness hotness,
+                                                  const int* off, int E,
                                                   TileEntry* tiles13, int32_t* ntiles13, int bm13,
                                                   TileEntry* tiles2, int32_t* ntiles2, int bm2,
                                                   int* scan) {
@@ -186,12 +202,8 @@ __device__ __forceinline__ void write_tile_tables(const DevHandle* table, WaveMa
   // DynaExq hotness from the router trace: decayed count of routes per expert
   if (hotness.hot && tid < E)
     hotness.hot[tid] = hotness.decay * hotness.hot[tid] + (float)(off[tid + 1] - off[tid]);
-  const int e = min(tid, E - 1);
-  // wave mode: only experts mapped to a resident slot get tiles, with the
-  // slot's weights (ExactMoE 3.4: the other experts map to the sentinel)
-  const int slot = wave.slot_map ? wave.slot_map[e] : 0;
-  const bool active = !wave.slot_map || (slot >= 0 && slot < E);
-  const DevHandle h = wave.slot_map ? wave.slots[active ? slot : 0] : table[e];
+  const DevHandle& h = src.h;
+  const bool active = src.active;
   for (int gemm = 0; gemm < 2; ++gemm) {
     const int bm = gemm == 0 ? bm13 : bm2;
     TileEntry* tiles = gemm == 0 ? tiles13 : tiles2;
@@ -234,6 +246,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = (T + 15) / 16;
   const int tb = min(T, wave * chunk), te = min(T, tb + chunk);
+  const TileSource src = tile_source(table, wmap, E);
 
   for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
   __syncthreads();
@@ -275,7 +288,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
   __syncthreads();
 
-  write_tile_tables(table, wmap, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
 }
 
 // Rank pass of the multi-block grouping (large T).  Block c owns the 256
@@ -329,6 +342,8 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   __shared__ int off[kMaxExperts + 1];
   __shared__ int scan[16];
   const int tid = threadIdx.x, c = blockIdx.x;
+  TileSource src{};
+  if (c == 0) src = tile_source(table, wmap, E);   // block 0 writes the tile tables
   int total = 0;
   if (tid < E) {
     int b = 0, tot = 0;
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   }
   if (c != 0) return;
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
-  write_tile_tables(table, wmap, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
 }
 
 }  // namespace
