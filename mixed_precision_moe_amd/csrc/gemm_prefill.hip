@@ -222,13 +222,28 @@ __device__ __forceinline__ void dequant_b(const BDirect& raw, f16x8_t (&fb)[2][4
 // left unconstrained
 constexpr int wait_vmcnt(int n) { return n | (0x7 << 4) | (0xF << 8); }
 
+// Row-aware work of a tile with fewer than 256 rows (FULL = false; all
+// conditions wave-uniform): a wave issues the activation DMA only for its
+// 32-row slice of the panel if that holds a real row, and MFMAs (and operand
+// reads) only for its 64-row halves that hold one; a wave whose 128 rows are
+// all past the tile's count loads no weights.  The others' results are never
+// stored, so the skipped work changes no output.
+struct RowWork {
+  int rows;                       // real rows of the tile (1 .. 256)
+  __device__ bool dma(int wave) const { return 32 * wave < rows; }
+  __device__ bool blk(int wm, int i) const { return 128 * wm + 16 * i < rows; }
+  __device__ bool any(int wm) const { return 128 * wm < rows; }
+};
+
 // int4 tier: weights straight from memory into MFMA operands.
-template <bool GATE_UP>
+template <bool GATE_UP, bool FULL>
 __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, const uint8_t* blob,
                                                         const int (&arow)[4], int n_block,
-                                                        lds_u8* lds, f32x4_t (&acc)[8][4]) {
+                                                        lds_u8* lds, f32x4_t (&acc)[8][4],
+                                                        RowWork rw) {
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
+  const bool wave_b = FULL || rw.any(wm);               // this wave needs weights
   const int K = a.K, G = K / kGroup, KC = K / PBK;
   constexpr int kWaitVmcntB = wait_vmcnt(5);            // one chunk's weight loads per lane
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<MOE_TIER_INT4>(a.N, K));
@@ -257,12 +272,14 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   // weights of chunk c travel in register slot c % 2, two chunks ahead
   BDirect braw0, braw1;
   auto load_b = [&](int kc, BDirect& raw) {
+    if (!wave_b) return;
     const uint32_t block = (uint32_t)(quad * G + (kc >> 1)) * kBlk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) raw.w[j] = buffer_load8(rsrc, 16 * lane + 1024 * j, block + 8 * (kc & 1));
     raw.scale = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
   };
   auto dma_a = [&](int kc, int buf) {
+    if (!FULL && !rw.dma(wave)) return;
     lds_u8* dst = As(buf) + 4 * wave * 1024;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -274,14 +291,22 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   auto read_frags = [&](int buf, int ks) {
     const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
+    for (int h = 0; h < 2; ++h)
+      if (FULL || rw.blk(wm, 4 * h)) {
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i)
+          fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
+      }
   };
   auto mfma_block = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int h = 0; h < 2; ++h)
+      if (FULL || rw.blk(wm, 4 * h)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
+        for (int i = 4 * h; i < 4 * h + 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
+      }
   };
 
   // One chunk: its successor's activations stream into the other buffer by
@@ -294,7 +319,7 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   auto step = [&](int kc, BDirect& raw) {
     const int buf = kc & 1;
     dma_a(min(kc + 1, KC - 1), buf ^ 1);
-    dequant_b(raw, fb);
+    if (wave_b) dequant_b(raw, fb);
     load_b(min(kc + 2, KC - 1), raw);
     read_frags(buf, 0);
     read_frags(buf, 1);
@@ -321,10 +346,11 @@ constexpr int staged_loads() { return TIER == MOE_TIER_INT4 ? 5 : 4; }
 // int8 and bf16 tiers: the weights, two to four times the int4 bytes, are
 // staged once per block through LDS (dequantized by one thread per column and
 // k-step) instead of being fetched by both waves that share a column range.
-template <int TIER, bool GATE_UP>
+template <int TIER, bool GATE_UP, bool FULL>
 __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, const uint8_t* blob,
                                                  const int (&arow)[4], int n_block,
-                                                 lds_u8* lds, f32x4_t (&acc)[8][4]) {
+                                                 lds_u8* lds, f32x4_t (&acc)[8][4], RowWork rw) {
+  (void)rw;   // used only when FULL is false
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int K = a.K, G = K / kGroup, KC = K / PBK;
@@ -378,6 +404,7 @@ __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, co
     if constexpr (TIER == MOE_TIER_INT4) raw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
   };
   auto dma_a = [&](int kc, int buf) {
+    if (!FULL && !rw.dma(wave)) return;
     lds_u8* dst = As(buf) + 4 * wave * 1024;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -393,17 +420,25 @@ __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, co
     const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
     const lds_u8* Bw = Bs(buf) + (2 * 4 * wn + ks) * kFragBytes + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
+    for (int h = 0; h < 2; ++h)
+      if (FULL || rw.blk(wm, 4 * h)) {
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i)
+          fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
+      }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       fb[ks][j] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Bw + 2 * j * kFragBytes));
   };
   auto mfma_block = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int h = 0; h < 2; ++h)
+      if (FULL || rw.blk(wm, 4 * h)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
+        for (int i = 4 * h; i < 4 * h + 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
+      }
   };
 
   // One chunk: its successor's activations stream into the other buffer by
@@ -458,10 +493,18 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if constexpr (TIER == MOE_TIER_INT4)
-    prefill_mainloop_direct<GATE_UP>(a, blob, arow, n_block, plds, acc);
-  else
-    prefill_mainloop_staged<TIER, GATE_UP>(a, blob, arow, n_block, plds, acc);
+  // row-aware main loop for partial int4 tiles (the staged tiers always run
+  // the full tile: their row-aware variant does not fit the register budget)
+  const RowWork rw{te.rows};
+  const bool full = te.rows >= PBM;          // tile-uniform
+  if constexpr (TIER == MOE_TIER_INT4) {
+    if (full)
+      prefill_mainloop_direct<GATE_UP, true>(a, blob, arow, n_block, plds, acc, rw);
+    else
+      prefill_mainloop_direct<GATE_UP, false>(a, blob, arow, n_block, plds, acc, rw);
+  } else {
+    prefill_mainloop_staged<TIER, GATE_UP, true>(a, blob, arow, n_block, plds, acc, rw);
+  }
   const int col0 = n_block + 64 * wn;      // first packed column of this wave (one quad)
   if constexpr (GATE_UP) {
     // strips 0, 1 of the quad are gate, 2, 3 the matching up columns

@@ -84,12 +84,16 @@ def test_layer_mixed_tiers_small():
     _run(st)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 31, 33, 64, 65, 127, 128])
+@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 31, 33, 64, 65, 127, 128,
+                               129, 191, 255, 256, 257])
 def test_token_group_sizes(T):
     """All T tokens routed to experts 2 and 5 (large bias): one group of T rows
     per expert, T = 1..128 (the token-group sizes the ExactMoE kernel tests
-    cover, section 5.3), across the tile boundaries of both GEMMs."""
-    cfg = dataclasses.replace(inputs.get_config(1), max_tokens=128)
+    cover, section 5.3), across the tile boundaries of both GEMMs; past 32
+    routes per expert the large-batch kernel runs, whose partial tiles skip
+    the 16-row blocks and weight loads past the group (129..257: both halves
+    of the 256-row tile, a full tile, a full tile plus one row)."""
+    cfg = dataclasses.replace(inputs.get_config(1), max_tokens=300)
     b = np.zeros(8, np.float32)
     b[[2, 5]] = 100.0
     st = Setup(1, T=T, cfg=cfg, bias=b, tiers=np.array([2, 2, 2, 1, 2, 0, 2, 2]))
