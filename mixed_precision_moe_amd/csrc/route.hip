@@ -193,11 +193,22 @@ __device__ __forceinline__ TileSource tile_source(const DevHandle* table, WaveMa
   return TileSource{wave.slot_map ? wave.slots[active ? slot : 0] : table[e], active};
 }
 
+// Large-batch tile tables (bm >= kSortTilesMinBm) list every expert's full
+// tiles first (expert order), then the partial tiles by row count,
+// descending: the large-batch GEMMs process tiles in table order, so the
+// cheapest tiles (row-aware partial tiles) fill the GPU's last round.  The
+// order comes from a counting sort over the bm row counts (LDS histogram,
+// block scan, atomic placement); partial tiles with equal row counts may
+// land in either order, which changes no result (every tile writes only its
+// own rows).  hist[] is LDS scratch of kMaxTileRows ints.
+constexpr int kSortTilesMinBm = 64;
+constexpr int kMaxTileRows = 256;
+
 __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness hotness,
                                                   const int* off, int E,
                                                   TileEntry* tiles13, int32_t* ntiles13, int bm13,
                                                   TileEntry* tiles2, int32_t* ntiles2, int bm2,
-                                                  int* scan) {
+                                                  int* scan, int* hist) {
   const int tid = threadIdx.x;
   // DynaExq hotness from the router trace: decayed count of routes per expert
   if (hotness.hot && tid < E)
@@ -209,20 +220,41 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
     TileEntry* tiles = gemm == 0 ? tiles13 : tiles2;
     int32_t* ntiles = gemm == 0 ? ntiles13 : ntiles2;
     const int ce = tid < E && active ? off[tid + 1] - off[tid] : 0;
-    const int nt = (ce + bm - 1) / bm;
-    int tot = 0;
-    const int first = block_exclusive_scan(nt, scan, tot);
-    for (int i = 0; i < nt; ++i) {
+    auto put = [&](int at, int i, int rows) {
       TileEntry te2;
       te2.expert = tid;
       te2.row_start = off[tid] + i * bm;
-      te2.rows = min(bm, ce - i * bm);
+      te2.rows = rows;
       te2.tier = h.tier;
       te2.w = gemm == 0 ? h.w13 : h.w2;
       te2.pad = 0;
-      tiles[first + i] = te2;
+      tiles[at] = te2;
+    };
+    if (bm < kSortTilesMinBm || bm > kMaxTileRows) {   // block-uniform
+      const int nt = (ce + bm - 1) / bm;
+      int tot = 0;
+      const int first = block_exclusive_scan(nt, scan, tot);
+      for (int i = 0; i < nt; ++i) put(first + i, i, min(bm, ce - i * bm));
+      if (tid == 0) *ntiles = tot;
+    } else {
+      const int nfull = ce / bm, rem = ce - nfull * bm;
+      int nf = 0;
+      const int first = block_exclusive_scan(nfull, scan, nf);
+      for (int i = 0; i < nfull; ++i) put(first + i, i, bm);
+      const int key = bm - 1 - rem;                       // more rows first
+      if (tid < bm) hist[tid] = 0;
+      __syncthreads();
+      if (rem > 0) atomicAdd(&hist[key], 1);
+      __syncthreads();
+      const int cnt = tid < bm ? hist[tid] : 0;
+      int np = 0;
+      const int base = block_exclusive_scan(cnt, scan, np);   // its barriers order the read above
+      if (tid < bm) hist[tid] = base;
+      __syncthreads();
+      if (rem > 0) put(nf + atomicAdd(&hist[key], 1), nfull, rem);
+      if (tid == 0) *ntiles = nf + np;
+      __syncthreads();   // hist[] is reused by the next GEMM's table
     }
-    if (tid == 0) *ntiles = tot;
   }
 }
 
@@ -243,6 +275,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   int* cnt = lds;                 // [16][E]
   int* off = cnt + 16 * E;        // [E+1] exclusive scan of totals
   int* scan = off + E + 1;        // [1024] scan scratch
+  int* hist = off + E + 1 + 1024;  // [kMaxTileRows] tile-ordering histogram
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = (T + 15) / 16;
   const int tb = min(T, wave * chunk), te = min(T, tb + chunk);
@@ -288,7 +321,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
   __syncthreads();
 
-  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan, hist);
 }
 
 // Rank pass of the multi-block grouping (large T).  Block c owns the 256
@@ -341,6 +374,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   __shared__ int base[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int scan[16];
+  __shared__ int hist[kMaxTileRows];
   const int tid = threadIdx.x, c = blockIdx.x;
   TileSource src{};
   if (c == 0) src = tile_source(table, wmap, E);   // block 0 writes the tile tables
@@ -369,7 +403,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   }
   if (c != 0) return;
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
-  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan, hist);
 }
 
 }  // namespace
@@ -422,12 +456,12 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
                        tiles2, ntiles2, bm2);
     return hipGetLastError();
   }
-  const size_t lds = sizeof(int) * (16 * (size_t)E + E + 1 + 1024);
+  const size_t lds = sizeof(int) * (17 * (size_t)E + 1025 + kMaxTileRows);
   static bool attr_set = false;   // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB)
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(sizeof(int) * (16 * kMaxExperts + kMaxExperts + 1 + 1024)));
+                                             (int)(sizeof(int) * (17 * kMaxExperts + 1025 + kMaxTileRows)));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
