@@ -134,8 +134,17 @@ def cpu_baseline(cfg, tiers, x, wr, bias, min_seconds=10.0, max_seconds=30.0):
             if el >= min_seconds or el * (reps + 1) / reps > max_seconds:
                 break
     T = x.shape[0]
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(T * reps / el, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"{reps} full forward(s) of the same {T}-token batch (dequantize "
                       f"{touched.size} touched experts, route, expert FFNs, combine; "
                       f"quantization excluded); numpy float64, BLAS pool of {cores} threads",
