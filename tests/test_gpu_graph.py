@@ -1,6 +1,8 @@
 """A captured forward replays correctly: several replays of a HIP graph holding
 one layer forward, with eager work and synchronizations in between, each give
-the eager result byte for byte (decode and prefill paths)."""
+the eager result byte for byte: the decode path, the large-batch path with
+int4 and staged (int8/bf16) tiers, and at T = 2048 the MFMA router, the
+multi-block grouping and row-aware partial tiles."""
 
 import numpy as np
 import pytest
@@ -10,7 +12,7 @@ from tests._harness import Setup, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cid,T", [(2, 32), (1, 64)])
+@pytest.mark.parametrize("cid,T", [(2, 32), (1, 64), (3, 512), (4, 2048)])
 def test_graph_replay_matches_eager(cid, T):
     import torch
     st = Setup(cid, T=T)
