@@ -119,17 +119,22 @@ __device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>:
 // Decode kernel: few rows per expert (an M-tile of at most 16 routes), so the
 // cost is streaming the expert's weights from HBM.  A block of WAVES waves
 // owns one M-tile and WAVES * NS consecutive 16-column strips.  Its A rows
-// (only the tile's real rows, all of K) and their group sums are staged into
-// LDS once, while every wave already has its first weight loads in flight;
-// after that single barrier each wave streams its strips over the whole K with
-// the next D k-groups of weights and scales in flight, reading A fragments
-// from LDS (rows beyond the tile's count feed only rows that are never stored).  For a
-// gate/up matrix NS = 4 covers 32 gate and the matching 32 up columns.
+// (only the tile's real rows) and their group sums are staged into LDS one
+// K-chunk of at most kDecodeChunkK columns at a time (one chunk for K up to
+// that size), while every wave already has the chunk's first weight loads in
+// flight; after the chunk's barrier each wave streams its strips over the
+// chunk with the next D k-groups of weights and scales in flight, reading A
+// fragments from LDS (rows beyond the tile's count feed only rows that are
+// never stored).  For a gate/up matrix NS = 4 covers 32 gate and the
+// matching 32 up columns.
 // ---------------------------------------------------------------------------
 // s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 constexpr int kDecodeRows = 8;   // rows of an M-tile in the decode kernel (MFMA rows 8..15 are zero)
 constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
+constexpr int kDecodeChunkK = 4096;   // A columns staged per chunk (a multiple of kGroup)
+
+__host__ __device__ constexpr int decode_chunk_k(int K) { return K < kDecodeChunkK ? K : kDecodeChunkK; }
 
 template <int TIER, int NS, int WAVES, bool GATE_UP>
 __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEntry& te,
@@ -141,7 +146,8 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   constexpr int L = TR::kLoads;
   const int lane = threadIdx.x & 63;
   const int K = a.K, G = K / kGroup;
-  const int lda = K + 8;                      // LDS row stride (bf16)
+  const int KC = decode_chunk_k(K), GC = KC / kGroup;
+  const int lda = KC + 8;                     // LDS row stride (bf16)
   const int rows = te.rows;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_payload<TIER>(a.N, K));
   // The wave's NS strips are strips u0 .. u0+NS-1 of quad `quad` (NS divides 4).
@@ -167,39 +173,6 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
         sc[d] = make_uint2(buffer_load_u16(rsrc, scale_voff, block + 4096u), 0u);
     }
   };
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < G) issue(d, d);
-
-  // stage A rows and group sums of this tile (block-wide, once)
-  {
-    const int chunks = rows * (K / 8);
-    for (int c = threadIdx.x; c < chunks; c += 64 * WAVES) {
-      const int m = c / (K / 8), col = 8 * (c - m * (K / 8));
-      const int pos = te.row_start + m;
-      const uint16_t* src = GATE_UP ? a.a_src + (size_t)(a.sorted[pos] / a.top_k) * K + col
-                                    : a.a_src + (size_t)pos * K + col;
-      *reinterpret_cast<uint4*>(lds_a + m * lda + col) = *reinterpret_cast<const uint4*>(src);
-    }
-    if constexpr (TIER != MOE_TIER_BF16) {
-      for (int i = threadIdx.x; i < G * kRStride; i += 64 * WAVES) {
-        const int g = i / kRStride, m = i - g * kRStride;
-        float r = 0.0f;
-        if (m < rows) {
-          const int pos = te.row_start + m;
-          r = GATE_UP ? row_sum<true>(a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G, g)
-                      : row_sum<false>(a.rsum + (size_t)pos * (K / 32), g);
-        }
-        lds_r[i] = r;
-      }
-    }
-  }
-  // Drain every load before the barrier.  The staging loops above are skipped
-  // by waves without work; on that path the first weight loads would still be
-  // pending at the main loop, and the compiler's merged wait state then drains
-  // all loads at the top of every iteration instead of only the oldest group.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
 
   float row_scale[NS];
   if constexpr (TIER == MOE_TIER_INT8) {
@@ -212,13 +185,17 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   // accumulator rows that the epilogue never stores, so no lane is masked.
   const uint16_t* la = lds_a + (lane & 7) * lda + 8 * (lane >> 4);
 
+  // consume(g, d): k-group g (absolute), whose weights are in set d and whose
+  // A columns and group sums sit at chunk-relative group g - c0 in LDS
+  int c0 = 0;
   auto consume = [&](int g, int d) {
+    const int gl = g - c0;
     f32x4_t p[NS];
     if constexpr (TIER == MOE_TIER_BF16) {
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns) p[ns] = acc[ns];
     } else {
-      const float4 r4 = *reinterpret_cast<const float4*>(lds_r + g * kRStride + 4 * (lane >> 4));
+      const float4 r4 = *reinterpret_cast<const float4*>(lds_r + gl * kRStride + 4 * (lane >> 4));
       const f32x4_t init = {-TR::kOffset * r4.x, -TR::kOffset * r4.y, -TR::kOffset * r4.z,
                             -TR::kOffset * r4.w};
 #pragma unroll
@@ -226,7 +203,7 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     }
     bf16x8_t af[4];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) af[s4] = as_bf16x8(load_u32x4(la + kGroup * g + 32 * s4));
+    for (int s4 = 0; s4 < 4; ++s4) af[s4] = as_bf16x8(load_u32x4(la + kGroup * gl + 32 * s4));
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
@@ -248,32 +225,74 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     }
   };
 
-  // Steady state: every group consumed here has a successor D groups ahead, so
-  // the body is branch-free and each register set bb[d] keeps its role (no
-  // copies between loads in flight, which would force early waits).
-  int g0 = 0;
+  for (; c0 < G; c0 += GC) {
+    const int c1 = c0 + GC < G ? c0 + GC : G;   // this chunk: groups [c0, c1)
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (c0 + d < c1) issue(c0 + d, d);
+    if (c0 > 0) __syncthreads();   // every wave is done with the previous chunk's A
+
+    // stage this chunk's A columns and group sums (block-wide)
+    {
+      const int kc = (c1 - c0) * kGroup;
+      const int chunks = rows * (kc / 8);
+      for (int c = threadIdx.x; c < chunks; c += 64 * WAVES) {
+        const int m = c / (kc / 8), col = 8 * (c - m * (kc / 8));
+        const int pos = te.row_start + m;
+        const size_t kcol = (size_t)c0 * kGroup + col;
+        const uint16_t* src = GATE_UP ? a.a_src + (size_t)(a.sorted[pos] / a.top_k) * K + kcol
+                                      : a.a_src + (size_t)pos * K + kcol;
+        *reinterpret_cast<uint4*>(lds_a + m * lda + col) = *reinterpret_cast<const uint4*>(src);
+      }
+      if constexpr (TIER != MOE_TIER_BF16) {
+        for (int i = threadIdx.x; i < (c1 - c0) * kRStride; i += 64 * WAVES) {
+          const int gl = i / kRStride, m = i - gl * kRStride;
+          float r = 0.0f;
+          if (m < rows) {
+            const int pos = te.row_start + m;
+            r = GATE_UP ? row_sum<true>(a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G, c0 + gl)
+                        : row_sum<false>(a.rsum + (size_t)pos * (K / 32), c0 + gl);
+          }
+          lds_r[i] = r;
+        }
+      }
+    }
+    // Drain every load before the barrier.  The staging loops above are
+    // skipped by waves without work; on that path the first weight loads
+    // would still be pending at the main loop, and the compiler's merged wait
+    // state then drains all loads at the top of every iteration instead of
+    // only the oldest group.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+
+    // Steady state: every group consumed here has a successor D groups ahead
+    // in the chunk, so the body is branch-free and each register set bb[d]
+    // keeps its role (no copies between loads in flight, which would force
+    // early waits).
+    int g0 = c0;
 #pragma nounroll
-  for (; g0 + 2 * D <= G; g0 += D) {
+    for (; g0 + 2 * D <= c1; g0 += D) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      consume(g0 + d, d);
-      issue(g0 + d + D, d);
-      // keep the next group's math after this reload: otherwise the scheduler
-      // batches the math of all D groups ahead of every reload and the wave
-      // computes with no weight loads in flight
-      __builtin_amdgcn_sched_barrier(0);
+      for (int d = 0; d < D; ++d) {
+        consume(g0 + d, d);
+        issue(g0 + d + D, d);
+        // keep the next group's math after this reload: otherwise the
+        // scheduler batches the math of all D groups ahead of every reload
+        // and the wave computes with no weight loads in flight
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    // the chunk's last (fewer than 2D) groups
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (g0 + d < c1) {
+        consume(g0 + d, d);
+        if (g0 + d + D < c1) issue(g0 + d + D, d);
+      }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (g0 + D + d < c1) consume(g0 + D + d, d);
   }
-  // the last (fewer than 2D) groups
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (g0 + d < G) {
-      consume(g0 + d, d);
-      if (g0 + d + D < G) issue(g0 + d + D, d);
-    }
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (g0 + D + d < G) consume(g0 + D + d, d);
 }
 
 // Occupancy: three waves per SIMD for gate/up (K = H, long weight streams);
@@ -298,7 +317,7 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const int chunk = nb * WAVES + wave;       // this wave's group of NS strips
   const int strip0 = chunk * NS;
   uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
-  float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)kDecodeRows * (a.K + 8) * 2);
+  float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)kDecodeRows * (decode_chunk_k(a.K) + 8) * 2);
 
   f32x4_t acc[NS];
 #pragma unroll
@@ -357,7 +376,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
 }
 
 size_t decode_lds_bytes(int K) {
-  return (size_t)kDecodeRows * (K + 8) * 2 + (size_t)(K / kGroup) * kRStride * 4;
+  const int KC = decode_chunk_k(K);
+  return (size_t)kDecodeRows * (KC + 8) * 2 + (size_t)(KC / kGroup) * kRStride * 4;
 }
 
 template <int NS, bool GATE_UP>

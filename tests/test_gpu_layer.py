@@ -73,6 +73,23 @@ def test_layer_mixtral_prefill_sampled():
     _run(st, subset=sub, keep=False, runs=2)
 
 
+@pytest.mark.parametrize("T", [1, 32])
+def test_layer_mixtral_decode_sampled(T):
+    """Mixtral shape at decode sizes: the down GEMM's K = 14336 is staged in
+    four K-chunks (the last one partial), gate/up's K = 4096 in one."""
+    st = Setup(5, T=T)
+    sub = [0] if T == 1 else [0, 31]
+    _run(st, subset=sub, keep=False, runs=2)
+
+
+def test_layer_decode_ragged_k_chunks():
+    """Both decode GEMMs with K just past one staged chunk (hidden 4352 and
+    inter 4224: a last chunk of two k-groups and of one), over all tiers."""
+    c = dataclasses.replace(inputs.get_config(1), hidden=4352, inter=4224, n_experts=4,
+                            top_k=2, max_tokens=16)
+    _run(Setup(1, T=16, cfg=c, tiers=np.array([2, 1, 0, 2])), keep=False)
+
+
 @pytest.mark.parametrize("tier", [0, 1, 2])
 def test_layer_single_tier(tier):
     st = Setup(1, tiers=np.full(8, tier))
