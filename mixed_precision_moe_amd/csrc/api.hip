@@ -502,6 +502,11 @@ hipError_t enqueue_route(const Layer& L, WaveMap wave, Hotness hotness, const Ws
                                 at<float>(ws, p.xn2), at<float>(ws, p.wn2), ids, w, st.s);
     if (e != hipSuccess) return e;
     st.rec(1);
+  } else if (!reuse_topk && !logits && use_small_router(T, L.E, L.H)) {
+    // few tokens: logits, group sums and top k in one launch
+    e = launch_router_topk_small(x, wr, bias, T, L.H, L.E, L.k, r13, ids, w, st.s);
+    if (e != hipSuccess) return e;
+    st.rec(1);
   } else {
     float* z = logits ? logits : at<float>(ws, p.logits);
     if (!reuse_topk) {   // later waves of a layer call keep the first wave's routing

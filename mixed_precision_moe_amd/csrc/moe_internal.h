@@ -148,6 +148,19 @@ hipError_t launch_router_certified(const uint16_t* x, const uint16_t* wr, const 
                                    int32_t* ids, float* w, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t s);
+// Few tokens: logits (canonical order), the group sums r13 and the top k in
+// one launch, one block per token; the logits stay on chip.  Same ids,
+// weights and r13, bit for bit, as launch_router_logits + launch_topk.
+constexpr int kSmallRouteMaxT = 64;
+constexpr int kSmallRouteMaxE = 128;
+// Router weights one block streams: one CU reads 512 KiB (E 128, H 2048) in
+// about 11 us, slower than the two-kernel path's 9.7 us; 256 KiB takes 7.8 us
+// against 9.2.
+constexpr size_t kSmallRouteMaxBytes = 256 * 1024;
+bool use_small_router(int T, int E, int H);
+hipError_t launch_router_topk_small(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                    int T, int H, int E, int k, float* r13, int32_t* ids,
+                                    float* w, hipStream_t s);
 // Grouping: one workgroup for T <= kPermSmallT, else a rank pass and a
 // scatter pass over blocks of kPermChunk tokens (rank [T*k] and chunk_counts
 // [ceil(T / kPermChunk) * E] are workspace).

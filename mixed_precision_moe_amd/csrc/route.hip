@@ -19,6 +19,17 @@
 namespace moe {
 namespace {
 
+// Sum of the 128 activations of one k-group: each of 16 lanes adds its 8
+// values pairwise, then a shuffle tree over the 16 lanes.  Every routing path
+// uses this one order, so the group sums agree bit for bit between them.
+__device__ __forceinline__ float group_sum_16lanes(const u32x4 q) {
+  float v = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
+            (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+  return v;
+}
+
 // Block: 8 half-waves (256 threads) arranged 2 (token groups) x 4 (expert
 // groups).  Each half-wave owns TT tokens x TE experts; block tile is
 // (2*TT) tokens x (4*TE) experts.  The slab loop takes SG slabs per step.
@@ -85,11 +96,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
       if (do_r13) {
 #pragma unroll
         for (int a = 0; a < TT; ++a) {
-          const u32x4 q = xv[sg][a];
-          float v = (bf16lo_to_f32(q.x) + bf16hi_to_f32(q.x)) + (bf16lo_to_f32(q.y) + bf16hi_to_f32(q.y)) +
-                    (bf16lo_to_f32(q.z) + bf16hi_to_f32(q.z)) + (bf16lo_to_f32(q.w) + bf16hi_to_f32(q.w));
-#pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+          const float v = group_sum_16lanes(xv[sg][a]);
           const int t = t0 + a;
           if ((j & 15) == 0 && t < T) r13[(size_t)t * G + base / kGroup + (j >> 4)] = v;
         }
@@ -147,6 +154,97 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logi
     id[m] = ok ? e : kNoExpert;
   }
   topk_select_softmax<PER>(v, id, k, ids + (size_t)t * k, weights + (size_t)t * k);
+}
+
+// Few tokens: one block per token computes the token's E logits in the
+// canonical order (the chains and fold of router_logits_kernel), keeps them in
+// LDS, and its first wave selects the top k as topk_kernel does.  One launch
+// and no logits round trip through memory.  The token's activation row is
+// staged in LDS once; half-wave hw (of 32) owns experts hw + 32 b, b < TE,
+// with SG slabs of weight loads issued per step.
+constexpr int kSmallRouteMaxH = 8192;
+template <int PER, int TE, int SG>
+__global__ __launch_bounds__(1024) void router_topk_small_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    int H, int E, int k, float* __restrict__ r13, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kSmallRouteMaxH];
+  __shared__ float zs[64 * PER];
+  const int t = blockIdx.x;
+  const int j = threadIdx.x & 31, hw = threadIdx.x >> 5;
+  const uint16_t* xrow = x + (size_t)t * H;
+  for (int c = threadIdx.x; c < H / 8; c += 1024)
+    *reinterpret_cast<u32x4*>(xs + 8 * c) = load_u32x4(xrow + 8 * c);
+  __syncthreads();
+
+  if (hw < E) {   // half-waves with no expert skip the dot products
+    const uint16_t* wp[TE];
+#pragma unroll
+    for (int b = 0; b < TE; ++b) wp[b] = wr + (size_t)min(hw + 32 * b, E - 1) * H + 8 * j;
+    float acc[TE];
+#pragma unroll
+    for (int b = 0; b < TE; ++b) acc[b] = 0.0f;
+    const bool do_r13 = r13 != nullptr && hw == 0;
+    const int G = H / kGroup;
+    for (int base0 = 0; base0 < H; base0 += 256 * SG) {
+      u32x4 xv[SG], wv[SG][TE];
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        const int base = base0 + 256 * sg;
+#pragma unroll
+        for (int b = 0; b < TE; ++b) wv[sg][b] = base < H ? load_u32x4(wp[b] + base) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        const int base = base0 + 256 * sg;
+        xv[sg] = base < H ? *reinterpret_cast<const u32x4*>(xs + base + 8 * j) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int sg = 0; sg < SG; ++sg) {
+        const int base = base0 + 256 * sg;
+        if (base >= H) break;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const uint32_t dx = (&xv[sg].x)[r >> 1];
+          const float xf = (r & 1) ? bf16hi_to_f32(dx) : bf16lo_to_f32(dx);
+#pragma unroll
+          for (int b = 0; b < TE; ++b) {
+            const uint32_t d = (&wv[sg][b].x)[r >> 1];
+            const float wf = (r & 1) ? bf16hi_to_f32(d) : bf16lo_to_f32(d);
+            acc[b] = __builtin_fmaf(xf, wf, acc[b]);
+          }
+        }
+        if (do_r13) {
+          const float v = group_sum_16lanes(xv[sg]);
+          if ((j & 15) == 0) r13[(size_t)t * G + base / kGroup + (j >> 4)] = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int sh = 16; sh >= 1; sh >>= 1)
+#pragma unroll
+      for (int b = 0; b < TE; ++b) acc[b] = acc[b] + __shfl_down(acc[b], sh, 32);
+    if (j == 0) {
+#pragma unroll
+      for (int b = 0; b < TE; ++b) {
+        const int e = hw + 32 * b;
+        if (e < E) zs[e] = acc[b] + (bias ? bias[e] : 0.0f);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float v[PER];
+    int id[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = lane + 64 * m;
+      v[m] = e < E ? zs[e] : -INFINITY;
+      id[m] = e < E ? e : kNoExpert;
+    }
+    topk_select_softmax<PER>(v, id, k, ids + (size_t)t * k, weights + (size_t)t * k);
+  }
 }
 
 // Exclusive prefix sum over the 1024 threads of a block; also returns the total.
@@ -421,6 +519,27 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const flo
     hipLaunchKernelGGL((router_logits_kernel<TT, TE, 1>), grid, dim3(256), 0, s, x, wr, bias, T, H,
                        E, logits, r13);
   }
+  return hipGetLastError();
+}
+
+bool use_small_router(int T, int E, int H) {
+  return T <= kSmallRouteMaxT && E <= kSmallRouteMaxE && H <= kSmallRouteMaxH &&
+         (size_t)E * H * 2 <= kSmallRouteMaxBytes;
+}
+
+hipError_t launch_router_topk_small(const uint16_t* x, const uint16_t* wr, const float* bias,
+                                    int T, int H, int E, int k, float* r13, int32_t* ids,
+                                    float* w, hipStream_t s) {
+  if (!use_small_router(T, E, H)) return hipErrorInvalidValue;
+  if (E <= 32)
+    hipLaunchKernelGGL((router_topk_small_kernel<1, 1, 8>), dim3(T), dim3(1024), 0, s, x, wr, bias,
+                       H, E, k, r13, ids, w);
+  else if (E <= 64)
+    hipLaunchKernelGGL((router_topk_small_kernel<1, 2, 8>), dim3(T), dim3(1024), 0, s, x, wr, bias,
+                       H, E, k, r13, ids, w);
+  else
+    hipLaunchKernelGGL((router_topk_small_kernel<2, 4, 4>), dim3(T), dim3(1024), 0, s, x, wr, bias,
+                       H, E, k, r13, ids, w);
   return hipGetLastError();
 }
 

@@ -1,6 +1,8 @@
 """GPU routing vs the oracle: logits, ids, offsets, permutation bit-exact;
 weights within 1e-6 (ExactMoE section 3.1 router and TopK; section 3.4 grouping)."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -73,6 +75,52 @@ def _route_np(layer, st, want_logits):
     got = {k: v.cpu().numpy() for k, v in layer.route(x, wr, b, want_logits=want_logits).items()}
     torch.cuda.synchronize()
     return got
+
+
+def _tie_rows(st):
+    wr = st.wr.copy()
+    wr[5] = wr[2]
+    wr[7] = wr[2]
+    wr[6] = wr[1]
+    st.wr = wr
+
+
+def _big_bias(st):
+    b = np.zeros(st.E, np.float32)
+    b[np.arange(st.k) * (st.E // st.k)] = 1000.0
+    st.bias = b
+
+
+def _small_cfg(E, H, k):
+    return dataclasses.replace(inputs.get_config(1), hidden=H, n_experts=E, top_k=k,
+                               max_tokens=64)
+
+
+@pytest.mark.parametrize("cid,T,mutate,shape", [
+    (6, 32, None, None), (6, 1, None, None), (6, 63, None, None), (6, 17, _big_bias, None),
+    (5, 7, None, None), (5, 64, None, None), (1, 64, _tie_rows, None), (1, 37, None, None),
+    (1, 1, _tie_rows, None), (1, 64, None, (128, 1024, 8)), (1, 33, _big_bias, (128, 1024, 8)),
+    (1, 20, None, (100, 768, 6)), (1, 64, None, (33, 2048, 4)), (1, 5, None, (32, 4096, 3))])
+def test_small_router_matches_canonical(cid, T, mutate, shape):
+    """Few tokens, no logits output, router weights up to 256 KiB: one block
+    per token computes the logits in the canonical order and takes the top k
+    on chip.  Same routing bit for bit as the logits + top-k kernels (ids,
+    weights, offsets, permutation) and the oracle's: E = 8, 32, 33, 64, 100,
+    128 (each expert-per-half-wave and expert-per-lane bound, full and
+    ragged); one token; exact ties; forced experts."""
+    st = Setup(cid, T=T) if shape is None else Setup(cid, T=T, cfg=_small_cfg(*shape))
+    if mutate is not None:
+        mutate(st)
+    layer = st.gpu_layer(experts=[0])
+    log(f"small route cfg{cid} T={T} E={st.E} k={st.k}")
+    fast = _route_np(layer, st, False)
+    canon = _route_np(layer, st, True)
+    for key in ("ids", "offsets", "sorted_routes", "route_pos"):
+        assert np.array_equal(fast[key], canon[key]), key
+    assert np.array_equal(fast["weights"].view(np.uint32), canon["weights"].view(np.uint32))
+    ref = oracle.route(st.x, st.wr, st.bias, st.k)
+    assert np.array_equal(fast["ids"], ref["ids"])
+    assert np.max(np.abs(fast["weights"] - ref["weights"])) <= 1e-6
 
 
 def _mfma_layer(st):
