@@ -32,6 +32,7 @@
 // the accumulator of lane l holds rows 4*(l/16) + i, column l%16.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_util.h"
@@ -136,7 +137,7 @@ constexpr int kDecodeChunkK = 4096;   // A columns staged per chunk (a multiple 
 
 __host__ __device__ constexpr int decode_chunk_k(int K) { return K < kDecodeChunkK ? K : kDecodeChunkK; }
 
-template <int TIER, int NS, int WAVES, bool GATE_UP>
+template <int TIER, int NS, int WAVES, bool GATE_UP, bool KSPLIT>
 __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEntry& te,
                                                 const uint8_t* blob, int strip0, uint16_t* lds_a,
                                                 float* lds_r, f32x4_t (&acc)[NS]) {
@@ -225,33 +226,48 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     }
   };
 
+  // K split over the block's waves: wave w takes k-groups [G w / WAVES,
+  // G (w + 1) / WAVES) of the block's strips
+  int g_lo = 0, g_hi = G;
+  if constexpr (KSPLIT) {
+    const int w = uniform(threadIdx.x >> 6);
+    g_lo = G * w / WAVES;
+    g_hi = G * (w + 1) / WAVES;
+  }
   for (; c0 < G; c0 += GC) {
-    const int c1 = c0 + GC < G ? c0 + GC : G;   // this chunk: groups [c0, c1)
+    int c1 = c0 + GC < G ? c0 + GC : G;   // this chunk: groups [c0, c1)
+    const int cs = c0;                    // the chunk's first group (its LDS origin)
+    int w0 = c0;                          // this wave's groups of the chunk: [w0, c1)
+    if constexpr (KSPLIT) {
+      w0 = cs > g_lo ? cs : g_lo;
+      c1 = c1 < g_hi ? c1 : g_hi;
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (c0 + d < c1) issue(c0 + d, d);
+      if (w0 + d < c1) issue(w0 + d, d);
     if (c0 > 0) __syncthreads();   // every wave is done with the previous chunk's A
 
     // stage this chunk's A columns and group sums (block-wide)
     {
-      const int kc = (c1 - c0) * kGroup;
+      const int ce = cs + GC < G ? cs + GC : G;
+      const int kc = (ce - cs) * kGroup;
       const int chunks = rows * (kc / 8);
       for (int c = threadIdx.x; c < chunks; c += 64 * WAVES) {
         const int m = c / (kc / 8), col = 8 * (c - m * (kc / 8));
         const int pos = te.row_start + m;
-        const size_t kcol = (size_t)c0 * kGroup + col;
+        const size_t kcol = (size_t)cs * kGroup + col;
         const uint16_t* src = GATE_UP ? a.a_src + (size_t)(a.sorted[pos] / a.top_k) * K + kcol
                                       : a.a_src + (size_t)pos * K + kcol;
         *reinterpret_cast<uint4*>(lds_a + m * lda + col) = *reinterpret_cast<const uint4*>(src);
       }
       if constexpr (TIER != MOE_TIER_BF16) {
-        for (int i = threadIdx.x; i < (c1 - c0) * kRStride; i += 64 * WAVES) {
+        for (int i = threadIdx.x; i < (ce - cs) * kRStride; i += 64 * WAVES) {
           const int gl = i / kRStride, m = i - gl * kRStride;
           float r = 0.0f;
           if (m < rows) {
             const int pos = te.row_start + m;
-            r = GATE_UP ? row_sum<true>(a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G, c0 + gl)
-                        : row_sum<false>(a.rsum + (size_t)pos * (K / 32), c0 + gl);
+            r = GATE_UP ? row_sum<true>(a.rsum + (size_t)(a.sorted[pos] / a.top_k) * G, cs + gl)
+                        : row_sum<false>(a.rsum + (size_t)pos * (K / 32), cs + gl);
           }
           lds_r[i] = r;
         }
@@ -269,7 +285,7 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     // in the chunk, so the body is branch-free and each register set bb[d]
     // keeps its role (no copies between loads in flight, which would force
     // early waits).
-    int g0 = c0;
+    int g0 = w0;
 #pragma nounroll
     for (; g0 + 2 * D <= c1; g0 += D) {
 #pragma unroll
@@ -298,7 +314,10 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 // Occupancy: three waves per SIMD for gate/up (K = H, long weight streams);
 // four for down, whose short K (I) makes more, shorter waves, all of which
 // then fit in one round at the decode workloads.
-template <int NS, int WAVES, bool GATE_UP>
+// KSPLIT (few tiles, so few waves for the GPU): the block's waves share its
+// NS strips and split K; their partial sums meet in LDS, added in wave order,
+// and wave 0 runs the epilogue.
+template <int NS, int WAVES, bool GATE_UP, bool KSPLIT>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 3 : 4, GATE_UP ? 3 : 4)))
 void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
@@ -314,7 +333,7 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   te.tier = uniform(te.tier);
   te.w = uniform_ptr(te.w);
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int chunk = nb * WAVES + wave;       // this wave's group of NS strips
+  const int chunk = KSPLIT ? nb : nb * WAVES + wave;   // this wave's group of NS strips
   const int strip0 = chunk * NS;
   uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
   float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)kDecodeRows * (decode_chunk_k(a.K) + 8) * 2);
@@ -325,14 +344,32 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const uint8_t* blob = te.w;
   switch (te.tier) {
     case MOE_TIER_INT4:
-      decode_mainloop<MOE_TIER_INT4, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
+      decode_mainloop<MOE_TIER_INT4, NS, WAVES, GATE_UP, KSPLIT>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
     case MOE_TIER_INT8:
-      decode_mainloop<MOE_TIER_INT8, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
+      decode_mainloop<MOE_TIER_INT8, NS, WAVES, GATE_UP, KSPLIT>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
     default:
-      decode_mainloop<MOE_TIER_BF16, NS, WAVES, GATE_UP>(a, te, blob, strip0, lds_a, lds_r, acc);
+      decode_mainloop<MOE_TIER_BF16, NS, WAVES, GATE_UP, KSPLIT>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
+  }
+  if constexpr (KSPLIT) {
+    static_assert(WAVES >= 2, "a split needs several waves");
+    float* red = reinterpret_cast<float*>(dyn_lds);   // [WAVES - 1][NS * 4][64]
+    __syncthreads();                                  // every wave is done with A in LDS
+    if (wave > 0) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[((wave - 1) * NS * 4 + ns * 4 + i) * 64 + lane] = acc[ns][i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w = 1; w < WAVES; ++w)
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ns][i] += red[((w - 1) * NS * 4 + ns * 4 + i) * 64 + lane];
   }
 
   if constexpr (GATE_UP) {
@@ -375,28 +412,34 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   }
 }
 
-size_t decode_lds_bytes(int K) {
+size_t decode_lds_bytes(int K, int NS, int WAVES, bool ksplit) {
   const int KC = decode_chunk_k(K);
-  return (size_t)kDecodeRows * (KC + 8) * 2 + (size_t)(KC / kGroup) * kRStride * 4;
+  const size_t stage = (size_t)kDecodeRows * (KC + 8) * 2 + (size_t)(KC / kGroup) * kRStride * 4;
+  const size_t red = ksplit ? (size_t)(WAVES - 1) * NS * 4 * 64 * 4 : 0;
+  return stage > red ? stage : red;
 }
 
+// Below this many waves (one per 64 output columns of every tile, tiles
+// estimated as min(E, T k)) the decode GEMMs split K over a block's waves.
+constexpr int kDecodeSplitWaves = 1024;
+
 template <int NS, bool GATE_UP>
-hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s, KernelTimer kt) {
-  // waves per block: as many strips of one tile as divide N evenly, up to 8
-  const int strips = a.N / 16;
-  const int chunks = strips / NS;
-  const size_t lds = decode_lds_bytes(a.K);
-  static bool attr_set[2] = {false, false};
-  auto run = [&](auto waves_c) -> hipError_t {
-    constexpr int W = decltype(waves_c)::value;
-    auto kern = gemm_decode_kernel<NS, W, GATE_UP>;
-    if (!attr_set[W == 8]) {
+hipError_t launch_decode(const GemmArgs& a, int max_tiles, bool ksplit, hipStream_t s,
+                         KernelTimer kt) {
+  constexpr int W = 4;
+  const int chunks = a.N / 16 / NS;   // groups of NS strips; N is a multiple of 256
+  const size_t lds = decode_lds_bytes(a.K, NS, W, ksplit);
+  auto run = [&](auto split_c) -> hipError_t {
+    constexpr bool KS = decltype(split_c)::value;
+    auto kern = gemm_decode_kernel<NS, W, GATE_UP, KS>;
+    static bool attr_set = false;
+    if (!attr_set) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
       if (e != hipSuccess) return e;
-      attr_set[W == 8] = true;
+      attr_set = true;
     }
-    const int bpt = chunks / W;
+    const int bpt = KS ? chunks : chunks / W;
     if (kt.start || kt.stop)
       hipExtLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), (uint32_t)lds, s, kt.start,
                             kt.stop, 0, a, bpt);
@@ -404,7 +447,12 @@ hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t s, Kernel
       hipLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), lds, s, a, bpt);
     return hipGetLastError();
   };
-  return run(std::integral_constant<int, 4>{});   // N is a multiple of 256: chunks % 4 == 0
+  return ksplit ? run(std::true_type{}) : run(std::false_type{});
+}
+
+bool decode_split_k(const Layer& L, int T, int N) {
+  const long tiles = std::min<long>(L.E, (long)T * L.k);
+  return tiles * (N / 64) < kDecodeSplitWaves;
 }
 
 
@@ -472,7 +520,6 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
                          const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
                          int max_tiles, const float* r13, uint16_t* act, float* r2,
                          hipStream_t s, KernelTimer kt) {
-  (void)T;
   GemmArgs a{};
   a.tiles = tiles;
   a.ntiles = ntiles;
@@ -486,14 +533,13 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.r2 = r2;
   a.I = L.I;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, true>(a, max_tiles, s, kt);
+  return launch_decode<4, true>(a, max_tiles, decode_split_k(L, T, a.N), s, kt);
 }
 
 hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
                         const int32_t* sorted, const float* topk_w, const TileEntry* tiles,
                         const int32_t* ntiles, int max_tiles, const float* r2, float* rows,
                         hipStream_t s) {
-  (void)T;
   GemmArgs a{};
   a.tiles = tiles;
   a.ntiles = ntiles;
@@ -506,7 +552,8 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.topk_w = topk_w;
   a.rows = rows;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, false>(a, max_tiles, s, KernelTimer{nullptr, nullptr});
+  return launch_decode<4, false>(a, max_tiles, decode_split_k(L, T, a.N), s,
+                                 KernelTimer{nullptr, nullptr});
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
