@@ -145,12 +145,12 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ logi
   const float* z = logits + (size_t)t * E;
   float v[PER];
   int id[PER];
-  const int per = (E + 63) / 64;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
+  for (int m = 0; m < PER; ++m) {   // clamped loads: all issued back to back, no branches
     const int e = lane + 64 * m;
-    const bool ok = m < per && e < E;
-    v[m] = ok ? z[e] : -INFINITY;
+    const bool ok = e < E;
+    const float ze = z[ok ? e : E - 1];
+    v[m] = ok ? ze : -INFINITY;
     id[m] = ok ? e : kNoExpert;
   }
   topk_select_softmax<PER>(v, id, k, ids + (size_t)t * k, weights + (size_t)t * k);
