@@ -131,13 +131,19 @@ __device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>:
 // ---------------------------------------------------------------------------
 // s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
-constexpr int kDecodeRows = 8;   // rows of an M-tile in the decode kernel (MFMA rows 8..15 are zero)
+// Rows of an M-tile in the decode kernel: ROWS = 8 (MFMA rows 8..15 are
+// copies) or 16 (all MFMA rows), chosen per forward from the mean rows per
+// expert.
+constexpr int kDecodeRowsMax = 16;
 constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
-constexpr int kDecodeChunkK = 4096;   // A columns staged per chunk (a multiple of kGroup)
+// A columns staged per chunk (multiples of kGroup): 4096 for 8-row tiles;
+// 1024 for 16-row tiles, so that a chunk stays near 33 KB of LDS and four
+// blocks fit a CU
+__host__ __device__ constexpr int decode_chunk_k(int K, int rows) {
+  return K < (rows == 8 ? 4096 : 1024) ? K : (rows == 8 ? 4096 : 1024);
+}
 
-__host__ __device__ constexpr int decode_chunk_k(int K) { return K < kDecodeChunkK ? K : kDecodeChunkK; }
-
-template <int TIER, int NS, int WAVES, bool GATE_UP, bool KSPLIT>
+template <int TIER, int NS, int WAVES, bool GATE_UP, bool KSPLIT, int ROWS>
 __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEntry& te,
                                                 const uint8_t* blob, int strip0, uint16_t* lds_a,
                                                 float* lds_r, f32x4_t (&acc)[NS]) {
@@ -147,7 +153,7 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   constexpr int L = TR::kLoads;
   const int lane = threadIdx.x & 63;
   const int K = a.K, G = K / kGroup;
-  const int KC = decode_chunk_k(K), GC = KC / kGroup;
+  const int KC = decode_chunk_k(K, ROWS), GC = KC / kGroup;
   const int lda = KC + 8;                     // LDS row stride (bf16)
   const int rows = te.rows;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, blob_payload<TIER>(a.N, K));
@@ -181,10 +187,10 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, u0 + ns);
   }
-  // A fragments: lane l reads LDS row l % 8.  MFMA rows 8..15 (and rows at or
-  // beyond the tile's count) then hold copies or stale data; they only feed
-  // accumulator rows that the epilogue never stores, so no lane is masked.
-  const uint16_t* la = lds_a + (lane & 7) * lda + 8 * (lane >> 4);
+  // A fragments: lane l reads LDS row l % ROWS.  MFMA rows ROWS..15 (and rows
+  // at or beyond the tile's count) then hold copies or stale data; they only
+  // feed accumulator rows that the epilogue never stores, so no lane is masked.
+  const uint16_t* la = lds_a + (lane & (ROWS - 1)) * lda + 8 * (lane >> 4);
 
   // consume(g, d): k-group g (absolute), whose weights are in set d and whose
   // A columns and group sums sit at chunk-relative group g - c0 in LDS
@@ -226,21 +232,17 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
     }
   };
 
-  // K split over the block's waves: wave w takes k-groups [G w / WAVES,
-  // G (w + 1) / WAVES) of the block's strips
-  int g_lo = 0, g_hi = G;
-  if constexpr (KSPLIT) {
-    const int w = uniform(threadIdx.x >> 6);
-    g_lo = G * w / WAVES;
-    g_hi = G * (w + 1) / WAVES;
-  }
   for (; c0 < G; c0 += GC) {
     int c1 = c0 + GC < G ? c0 + GC : G;   // this chunk: groups [c0, c1)
     const int cs = c0;                    // the chunk's first group (its LDS origin)
     int w0 = c0;                          // this wave's groups of the chunk: [w0, c1)
     if constexpr (KSPLIT) {
-      w0 = cs > g_lo ? cs : g_lo;
-      c1 = c1 < g_hi ? c1 : g_hi;
+      // K split over the block's waves inside every chunk: wave w takes the
+      // chunk's groups [n w / WAVES, n (w + 1) / WAVES), n = c1 - c0, so all
+      // waves work between any two of the chunk barriers
+      const int w = uniform(threadIdx.x >> 6), n = c1 - cs;
+      w0 = cs + n * w / WAVES;
+      c1 = cs + n * (w + 1) / WAVES;
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)
@@ -315,9 +317,9 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 // four for down, whose short K (I) makes more, shorter waves, all of which
 // then fit in one round at the decode workloads.
 // KSPLIT (few tiles, so few waves for the GPU): the block's waves share its
-// NS strips and split K; their partial sums meet in LDS, added in wave order,
-// and wave 0 runs the epilogue.
-template <int NS, int WAVES, bool GATE_UP, bool KSPLIT>
+// NS strips and split every staged K-chunk; their partial sums meet in LDS,
+// added in wave order, and wave 0 runs the epilogue.
+template <int NS, int WAVES, bool GATE_UP, bool KSPLIT, int ROWS>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 3 : 4, GATE_UP ? 3 : 4)))
 void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
@@ -336,7 +338,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const int chunk = KSPLIT ? nb : nb * WAVES + wave;   // this wave's group of NS strips
   const int strip0 = chunk * NS;
   uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
-  float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)kDecodeRows * (decode_chunk_k(a.K) + 8) * 2);
+  static_assert(ROWS == 8 || ROWS == 16, "an M-tile is 8 or 16 rows");
+  float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)ROWS * (decode_chunk_k(a.K, ROWS) + 8) * 2);
 
   f32x4_t acc[NS];
 #pragma unroll
@@ -344,13 +347,13 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const uint8_t* blob = te.w;
   switch (te.tier) {
     case MOE_TIER_INT4:
-      decode_mainloop<MOE_TIER_INT4, NS, WAVES, GATE_UP, KSPLIT>(a, te, blob, strip0, lds_a, lds_r, acc);
+      decode_mainloop<MOE_TIER_INT4, NS, WAVES, GATE_UP, KSPLIT, ROWS>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
     case MOE_TIER_INT8:
-      decode_mainloop<MOE_TIER_INT8, NS, WAVES, GATE_UP, KSPLIT>(a, te, blob, strip0, lds_a, lds_r, acc);
+      decode_mainloop<MOE_TIER_INT8, NS, WAVES, GATE_UP, KSPLIT, ROWS>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
     default:
-      decode_mainloop<MOE_TIER_BF16, NS, WAVES, GATE_UP, KSPLIT>(a, te, blob, strip0, lds_a, lds_r, acc);
+      decode_mainloop<MOE_TIER_BF16, NS, WAVES, GATE_UP, KSPLIT, ROWS>(a, te, blob, strip0, lds_a, lds_r, acc);
       break;
   }
   if constexpr (KSPLIT) {
@@ -412,9 +415,9 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   }
 }
 
-size_t decode_lds_bytes(int K, int NS, int WAVES, bool ksplit) {
-  const int KC = decode_chunk_k(K);
-  const size_t stage = (size_t)kDecodeRows * (KC + 8) * 2 + (size_t)(KC / kGroup) * kRStride * 4;
+size_t decode_lds_bytes(int K, int rows, int NS, int WAVES, bool ksplit) {
+  const int KC = decode_chunk_k(K, rows);
+  const size_t stage = (size_t)rows * (KC + 8) * 2 + (size_t)(KC / kGroup) * kRStride * 4;
   const size_t red = ksplit ? (size_t)(WAVES - 1) * NS * 4 * 64 * 4 : 0;
   return stage > red ? stage : red;
 }
@@ -424,14 +427,15 @@ size_t decode_lds_bytes(int K, int NS, int WAVES, bool ksplit) {
 constexpr int kDecodeSplitWaves = 1024;
 
 template <int NS, bool GATE_UP>
-hipError_t launch_decode(const GemmArgs& a, int max_tiles, bool ksplit, hipStream_t s,
+hipError_t launch_decode(const GemmArgs& a, int max_tiles, int rows, bool ksplit, hipStream_t s,
                          KernelTimer kt) {
   constexpr int W = 4;
   const int chunks = a.N / 16 / NS;   // groups of NS strips; N is a multiple of 256
-  const size_t lds = decode_lds_bytes(a.K, NS, W, ksplit);
-  auto run = [&](auto split_c) -> hipError_t {
+  const size_t lds = decode_lds_bytes(a.K, rows, NS, W, ksplit);
+  auto run = [&](auto split_c, auto rows_c) -> hipError_t {
     constexpr bool KS = decltype(split_c)::value;
-    auto kern = gemm_decode_kernel<NS, W, GATE_UP, KS>;
+    constexpr int RW = decltype(rows_c)::value;
+    auto kern = gemm_decode_kernel<NS, W, GATE_UP, KS, RW>;
     static bool attr_set = false;
     if (!attr_set) {
       const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -447,7 +451,11 @@ hipError_t launch_decode(const GemmArgs& a, int max_tiles, bool ksplit, hipStrea
       hipLaunchKernelGGL(kern, dim3(max_tiles * bpt), dim3(64 * W), lds, s, a, bpt);
     return hipGetLastError();
   };
-  return ksplit ? run(std::true_type{}) : run(std::false_type{});
+  using R8 = std::integral_constant<int, 8>;
+  using R16 = std::integral_constant<int, 16>;
+  if (rows == 8) return ksplit ? run(std::true_type{}, R8{}) : run(std::false_type{}, R8{});
+  if (rows == 16) return ksplit ? run(std::true_type{}, R16{}) : run(std::false_type{}, R16{});
+  return hipErrorInvalidValue;
 }
 
 bool decode_split_k(const Layer& L, int T, int N) {
@@ -506,12 +514,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
+constexpr double kDecodeRows8Max = 4.0;   // mean rows per expert up to which tiles are 8 rows
+
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
   const double rows_per_expert = (double)T * L.k / L.E;
-  const bool decode = rows_per_expert <= (double)kDecodeRows;
+  const bool decode = rows_per_expert <= (double)kDecodeRowsMax;
   p.kind = decode ? kGemmDecode : kGemmPrefill;
-  p.bm13 = decode ? kDecodeRows : 256;
+  // 8-row tiles while few experts overflow them (the LDS staging then fits
+  // any K up to 4096 in one chunk); 16-row tiles above
+  p.bm13 = decode ? (rows_per_expert <= kDecodeRows8Max ? 8 : 16) : 256;
   p.bm2 = p.bm13;
   return p;
 }
@@ -533,7 +545,7 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.r2 = r2;
   a.I = L.I;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, true>(a, max_tiles, decode_split_k(L, T, a.N), s, kt);
+  return launch_decode<4, true>(a, max_tiles, gp.bm13, decode_split_k(L, T, a.N), s, kt);
 }
 
 hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
@@ -552,7 +564,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.topk_w = topk_w;
   a.rows = rows;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, false>(a, max_tiles, decode_split_k(L, T, a.N), s,
+  return launch_decode<4, false>(a, max_tiles, gp.bm2, decode_split_k(L, T, a.N), s,
                                  KernelTimer{nullptr, nullptr});
 }
 

@@ -50,10 +50,20 @@ def test_layer_small_configs_full(cid):
     _run(Setup(cid))
 
 
-@pytest.mark.parametrize("T", [32, 512])
+@pytest.mark.parametrize("T", [32, 64, 128, 512])
 def test_layer_olmoe_full(T):
-    """The OLMoE-shaped layer (H 2048, E 64, top-8, I 1024): decode and prefill."""
+    """The OLMoE-shaped layer (H 2048, E 64, top-8, I 1024): decode with 8-row
+    tiles (T 32), with 16-row tiles staged in two K-chunks (T 64, 128: 8 and
+    16 rows per expert on average), and the large-batch path (T 512)."""
     _run(Setup(6, T=T))
+
+
+@pytest.mark.parametrize("T", [80, 200])
+def test_layer_mixed_tiers_16_row_tiles(T):
+    """Qwen3-30B shape with bf16, int8 and int4 experts and the Zipf bias at
+    5 and 12.5 rows per expert on average: 16-row decode tiles, hot experts
+    split over several tiles."""
+    _run(Setup(3, T=T), keep=False)
 
 
 @pytest.mark.parametrize("T", [1, 32, 256])
