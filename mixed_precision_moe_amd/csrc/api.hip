@@ -62,9 +62,9 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
   w.xn2 = take(sizeof(float) * (size_t)T * S);
   w.wn2 = take(sizeof(float) * (size_t)L.E * S);
   w.tiles13 = take(sizeof(TileEntry) * (size_t)(w.max_tiles13 > 0 ? w.max_tiles13 : 1));
-  w.ntiles13 = take(sizeof(int32_t));
+  w.ntiles13 = take(2 * sizeof(int32_t));   // [tile count, decode grouping flag]
   w.tiles2 = take(sizeof(TileEntry) * (size_t)(w.max_tiles2 > 0 ? w.max_tiles2 : 1));
-  w.ntiles2 = take(sizeof(int32_t));
+  w.ntiles2 = take(2 * sizeof(int32_t));
   w.r13 = take(sizeof(float) * T * (size_t)(L.H / kGroup));
   w.act = take(sizeof(uint16_t) * R * L.I);
   w.r2 = take(sizeof(float) * R * (L.I / 32));

@@ -333,7 +333,13 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
       int tot = 0;
       const int first = block_exclusive_scan(nt, scan, tot);
       for (int i = 0; i < nt; ++i) put(first + i, i, min(bm, ce - i * bm));
-      if (tid == 0) *ntiles = tot;
+      // ntiles[1]: some expert spans three or more tiles (the decode GEMMs
+      // then keep an expert's sub-tiles on one XCD)
+      const int many = __syncthreads_or(nt >= 3);
+      if (tid == 0) {
+        ntiles[0] = tot;
+        ntiles[1] = many;
+      }
     } else {
       const int nfull = ce / bm, rem = ce - nfull * bm;
       int nf = 0;
@@ -350,7 +356,10 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
       if (tid < bm) hist[tid] = base;
       __syncthreads();
       if (rem > 0) put(nf + atomicAdd(&hist[key], 1), nfull, rem);
-      if (tid == 0) *ntiles = nf + np;
+      if (tid == 0) {
+        ntiles[0] = nf + np;
+        ntiles[1] = 0;
+      }
       __syncthreads();   // hist[] is reused by the next GEMM's table
     }
   }
