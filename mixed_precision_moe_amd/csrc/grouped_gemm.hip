@@ -450,11 +450,11 @@ constexpr int kDecodeSplitWaves = 1024;
 template <int NS, bool GATE_UP>
 hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipStream_t s,
                          KernelTimer kt) {
-  // 16-row tiles: when an expert spans several tiles (a skewed router),
-  // group tiles by XCD (8 consecutive tiles per column block).  Without
-  // such experts the grouping only reshuffled the column blocks: 6.5% slower
-  // on the Mixtral shape at 16 routes per expert.
-  a.tile_group = rows == 16 ? kDecodeTileGroup : 0;
+  // When an expert spans several tiles (a skewed router), group tiles by
+  // XCD (8 consecutive tiles per column block).  Without such experts the
+  // grouping only reshuffled the column blocks: 6.5% slower on the Mixtral
+  // shape at 16 routes per expert.
+  a.tile_group = kDecodeTileGroup;
   constexpr int W = 4;
   const int chunks = a.N / 16 / NS;   // groups of NS strips; N is a multiple of 256
   const size_t lds = decode_lds_bytes(a.K, rows, NS, W, ksplit);

@@ -58,11 +58,11 @@ def test_layer_olmoe_full(T):
     _run(Setup(6, T=T))
 
 
-@pytest.mark.parametrize("T", [80, 200])
-def test_layer_mixed_tiers_16_row_tiles(T):
+@pytest.mark.parametrize("T", [40, 80, 200])
+def test_layer_mixed_tiers_skewed_decode(T):
     """Qwen3-30B shape with bf16, int8 and int4 experts and the Zipf bias at
-    5 and 12.5 rows per expert on average: 16-row decode tiles, hot experts
-    split over several tiles."""
+    2.5, 5 and 12.5 rows per expert on average: 8- and 16-row decode tiles,
+    hot experts spanning several tiles (their tiles grouped by XCD)."""
     _run(Setup(3, T=T), keep=False)
 
 
