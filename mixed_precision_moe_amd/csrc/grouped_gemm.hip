@@ -134,8 +134,11 @@ __device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>:
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // Rows of an M-tile in the decode kernel: ROWS = 8 (MFMA rows 8..15 are
 // copies) or 16 (all MFMA rows), chosen per forward from the mean rows per
-// expert.
+// expert.  Forwards take the decode kernels up to kDecodeRowsMax mean rows
+// per expert (kDecodeRowsMaxWide for layers with many experts, see
+// plan_gemm).
 constexpr int kDecodeRowsMax = 16;
+constexpr double kDecodeRowsMaxWide = 40.0;
 constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
 // A columns staged per chunk (multiples of kGroup): 4096 for 8-row tiles;
 // 1024 for 16-row tiles, so that a chunk stays near 33 KB of LDS and four
@@ -551,7 +554,16 @@ constexpr double kDecodeRows8Max = 4.0;   // mean rows per expert up to which ti
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
   const double rows_per_expert = (double)T * L.k / L.E;
-  const bool decode = rows_per_expert <= (double)kDecodeRowsMax;
+  // The large-batch gate/up kernel runs one 256 x 256 block per CU; with few
+  // rows per expert each block is latency-bound over K.  When its blocks
+  // (one per expert and 256 columns of 2I) fill the 256 CUs six or more
+  // times, those rounds cost more than streaming an expert's weights two or
+  // three times in 16-row decode tiles (Qwen3-80B shape, 20 and 30 rows per
+  // expert: 612 -> 420 and 643 -> 532 us); elsewhere the two paths met near
+  // 16 to 32 rows, and a Zipf-skewed router favoured the large-batch path.
+  const double rounds = (double)L.E * (2.0 * L.I / 256.0) / 256.0;
+  const double decode_max = rounds >= 6.0 ? kDecodeRowsMaxWide : (double)kDecodeRowsMax;
+  const bool decode = rows_per_expert <= decode_max;
   p.kind = decode ? kGemmDecode : kGemmPrefill;
   // 8-row tiles while few experts overflow them (the LDS staging then fits
   // any K up to 4096 in one chunk); 16-row tiles above

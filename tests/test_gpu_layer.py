@@ -71,6 +71,14 @@ def test_layer_qwen80b_sweep_full(T):
     _run(Setup(4, T=T), keep=False)
 
 
+def test_layer_qwen80b_1024_sampled():
+    """512 experts at 20 rows per expert on average: the decode kernels with
+    16-row tiles, experts spanning up to four tiles."""
+    st = Setup(4, T=1024)
+    sub = [0, 1, 511, 512, 1000, 1023]
+    _run(st, subset=sub, keep=False)
+
+
 def test_layer_qwen80b_4096_sampled():
     st = Setup(4, T=4096)
     sub = list(range(0, 4096, 97))[:40] + [4095]
