@@ -57,7 +57,7 @@ struct GemmArgs {
   // down epilogue
   const float* topk_w;       // [T*k] routing weights by route id
   float* rows;               // [T*k, H] fp32, grouped order
-  int tile_group;            // > 0 and ntiles[1] set: Q consecutive tiles of one column block share an XCD
+  int tile_group;            // non-zero and ntiles[1] set: kDecodeTileGroup consecutive tiles of one column block share an XCD
 };
 
 
@@ -137,6 +137,7 @@ constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // expert.  Forwards take the decode kernels up to kDecodeRowsMax mean rows
 // per expert (kDecodeRowsMaxWide for layers with many experts, see
 // plan_gemm).
+constexpr int kDecodeTileGroup = 8;   // tiles per column block kept on one XCD (grouped mapping)
 constexpr int kDecodeRowsMax = 16;
 constexpr double kDecodeRowsMaxWide = 40.0;
 constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
@@ -330,9 +331,11 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   static_assert(NS == 1 || NS == 2 || NS == 4, "a wave's strips lie in one quad");
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   int tile_idx, nb;
-  // ntiles[1]: the grouping kernel found an expert spanning three or more
-  // tiles (one scalar load with the tile count)
-  if (a.tile_group > 0 && uniform(a.ntiles[1]) != 0) {
+  // ntiles[0]: tile count; ntiles[1]: the grouping kernel found an expert
+  // spanning three or more tiles.  One 8-byte scalar load.
+  const int2 nt2 = *reinterpret_cast<const int2*>(a.ntiles);
+  const int ntiles = uniform(nt2.x);
+  if (a.tile_group && uniform(nt2.y) != 0) {
     // The hardware deals blocks to the 8 XCDs round robin.  The j-th block
     // an XCD receives is made logical block L = (j / Q) 8Q + xcd Q + j % Q
     // (a bijection on the grid, a multiple of 8Q blocks), and L covers
@@ -340,7 +343,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
     // Q consecutive tiles with the same columns run back to back on one
     // XCD, so the sub-tiles of an expert with many routes read its weights
     // through one L2.
-    const int Q = a.tile_group, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    constexpr int Q = kDecodeTileGroup;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int L = (j / Q) * 8 * Q + x * Q + j % Q;
     const int span = blocks_per_tile * Q, g = L / span, rem = L - g * span;
     nb = rem / Q;
@@ -349,7 +353,7 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
     tile_idx = blockIdx.x / blocks_per_tile;
     nb = blockIdx.x - tile_idx * blocks_per_tile;
   }
-  if (tile_idx >= uniform(*a.ntiles)) return;
+  if (tile_idx >= ntiles) return;
   TileEntry te = a.tiles[tile_idx];
   te.expert = uniform(te.expert);
   te.row_start = uniform(te.row_start);
@@ -444,8 +448,6 @@ size_t decode_lds_bytes(int K, int rows, int NS, int WAVES, bool ksplit) {
   return stage > red ? stage : red;
 }
 
-constexpr int kDecodeTileGroup = 8;
-
 // Below this many waves (one per 64 output columns of every tile, tiles
 // estimated as min(E, T k)) the decode GEMMs split K over a block's waves.
 constexpr int kDecodeSplitWaves = 1024;
@@ -457,7 +459,7 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
   // XCD (8 consecutive tiles per column block).  Without such experts the
   // grouping only reshuffled the column blocks: 6.5% slower on the Mixtral
   // shape at 16 routes per expert.
-  a.tile_group = kDecodeTileGroup;
+  a.tile_group = 1;
   constexpr int W = 4;
   const int chunks = a.N / 16 / NS;   // groups of NS strips; N is a multiple of 256
   const size_t lds = decode_lds_bytes(a.K, rows, NS, W, ksplit);
@@ -474,8 +476,8 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
     }
     const int bpt = KS ? chunks : chunks / W;
     unsigned blocks = (unsigned)(max_tiles * bpt);
-    if (a.tile_group > 0) {   // whole groups of Q tiles, then whole rounds of 8 groups
-      const unsigned Q = (unsigned)a.tile_group;
+    if (a.tile_group) {   // whole groups of Q tiles, then whole rounds of 8 groups
+      const unsigned Q = (unsigned)kDecodeTileGroup;
       blocks = (unsigned)((max_tiles + Q - 1) / Q * Q * bpt);
       blocks = (blocks + 8 * Q - 1) / (8 * Q) * (8 * Q);
     }

@@ -330,15 +330,17 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
     };
     if (bm < kSortTilesMinBm || bm > kMaxTileRows) {   // block-uniform
       const int nt = (ce + bm - 1) / bm;
+      // one scan gives each expert's first tile (low 20 bits; a decode table
+      // holds far fewer than 2^20 tiles) and the number of experts spanning
+      // three or more tiles (high bits)
       int tot = 0;
-      const int first = block_exclusive_scan(nt, scan, tot);
+      const int first = block_exclusive_scan(nt | (nt >= 3 ? 1 << 20 : 0), scan, tot) & 0xfffff;
       for (int i = 0; i < nt; ++i) put(first + i, i, min(bm, ce - i * bm));
       // ntiles[1]: some expert spans three or more tiles (the decode GEMMs
       // then keep an expert's sub-tiles on one XCD)
-      const int many = __syncthreads_or(nt >= 3);
       if (tid == 0) {
-        ntiles[0] = tot;
-        ntiles[1] = many;
+        ntiles[0] = tot & 0xfffff;
+        ntiles[1] = (tot >> 20) > 0 ? 1 : 0;
       }
     } else {
       const int nfull = ce / bm, rem = ce - nfull * bm;
