@@ -610,8 +610,15 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.topk_w = topk_w;
   a.rows = rows;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, false>(a, max_tiles, gp.bm2, decode_split_k(L, T, a.N), s,
-                                 KernelTimer{nullptr, nullptr});
+  const bool ks = decode_split_k(L, T, a.N);
+  // Very few column blocks even with split K (a wide-K, narrow-N down GEMM
+  // over one or two tiles, e.g. the Mixtral shape at one token): two strips
+  // per wave double the blocks.  Mixtral T = 1: 64.9 -> 61.3 us per layer;
+  // at 1280 or more waves it gained nothing, and at T = 4 it lost 7%.
+  const long est_tiles = std::min<long>(L.E, (long)T * L.k);
+  if (ks && est_tiles * (a.N / 64) * 4 < kDecodeSplitWaves)
+    return launch_decode<2, false>(a, max_tiles, gp.bm2, ks, s, KernelTimer{nullptr, nullptr});
+  return launch_decode<4, false>(a, max_tiles, gp.bm2, ks, s, KernelTimer{nullptr, nullptr});
 }
 
 hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
