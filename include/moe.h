@@ -209,8 +209,9 @@ int moe_plan_tiers(const float* hot, int32_t n_experts, const size_t* bytes_per_
 
 /* Router choice of later route and forward calls (moe_router_mode).  The
  * MFMA router needs workspace of its own: size the workspace after setting
- * the mode.  A decode-sized forward (a few routes per expert) always takes
- * the fixed-order kernel, which also produces the GEMM's group sums. */
+ * the mode.  A forward on the decode GEMMs that takes the MFMA router also
+ * runs one small pass over x for the GEMMs' group sums (the fixed-order
+ * kernel produces them on the way). */
 int moe_layer_set_router_mode(moe_layer_t layer, int32_t mode);
 
 /* Free the layer's device state.  The caller must have synchronized every

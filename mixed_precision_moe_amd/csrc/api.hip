@@ -497,9 +497,11 @@ hipError_t enqueue_route(const Layer& L, WaveMap wave, Hotness hotness, const Ws
   // Many tokens, logits not wanted (null): logits on MFMA, the top k taken
   // from the candidates the error bound leaves, recomputed in the canonical
   // order (the same routing bit for bit, see router_certified.hip).
-  if (!reuse_topk && !logits && !r13 && use_certified_router(L.router_mode, T, L.E, L.H)) {
+  if (!reuse_topk && !logits && use_certified_router(L.router_mode, T, L.E, L.H)) {
     e = launch_router_certified(x, wr, bias, T, L.H, L.E, L.k, at<float>(ws, p.logits),
                                 at<float>(ws, p.xn2), at<float>(ws, p.wn2), ids, w, st.s);
+    // the decode GEMMs' group sums, which the fixed-order kernel would write
+    if (e == hipSuccess && r13) e = launch_group_sums(x, T, L.H, r13, st.s);
     if (e != hipSuccess) return e;
     st.rec(1);
   } else if (!reuse_topk && !logits && use_small_router(T, L.E, L.H)) {

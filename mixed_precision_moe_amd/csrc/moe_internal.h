@@ -148,6 +148,9 @@ hipError_t launch_router_certified(const uint16_t* x, const uint16_t* wr, const 
                                    int32_t* ids, float* w, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t s);
+// R13 [T, H/128] alone (the fixed-order logits kernel also writes it), bit for
+// bit the same sums.
+hipError_t launch_group_sums(const uint16_t* x, int T, int H, float* r13, hipStream_t s);
 // Few tokens: logits (canonical order), the group sums r13 and the top k in
 // one launch, one block per token; the logits stay on chip.  Same ids,
 // weights and r13, bit for bit, as launch_router_logits + launch_topk.

@@ -247,6 +247,18 @@ __global__ __launch_bounds__(1024) void router_topk_small_kernel(
   }
 }
 
+// The decode GEMMs' group sums R13 [T, H/128] alone, for forwards whose
+// routing runs on the MFMA router: 16 consecutive threads hold one group,
+// summed in the same order as router_logits_kernel (bit-identical sums).
+// n8 is a multiple of 16, so the threads past the end leave in whole groups.
+__global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t* __restrict__ x,
+                                                         float* __restrict__ r13, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float g = group_sum_16lanes(load_u32x4(x + 8 * i));
+  if ((i & 15) == 0) r13[i / 16] = g;
+}
+
 // Exclusive prefix sum over the 1024 threads of a block; also returns the total.
 // Wave-level inclusive scan with shuffles, then one pass over the 16 wave totals.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
@@ -551,6 +563,13 @@ hipError_t launch_router_topk_small(const uint16_t* x, const uint16_t* wr, const
   else
     hipLaunchKernelGGL((router_topk_small_kernel<2, 4, 4>), dim3(T), dim3(1024), 0, s, x, wr, bias,
                        H, E, k, r13, ids, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_sums(const uint16_t* x, int T, int H, float* r13, hipStream_t s) {
+  const size_t n8 = (size_t)T * H / 8;   // a multiple of 16: H % 256 == 0
+  hipLaunchKernelGGL(group_sums_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x,
+                     r13, n8);
   return hipGetLastError();
 }
 
