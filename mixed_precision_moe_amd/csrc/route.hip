@@ -316,8 +316,8 @@ constexpr int kMaxTileRows = 256;
 
 __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness hotness,
                                                   const int* off, int E,
-                                                  TileEntry* tiles13, int32_t* ntiles13, int bm13,
-                                                  TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                                                  TileEntry* tiles13, int32_t* ntiles13,
+                                                  TileEntry* tiles2, int32_t* ntiles2, int bm,
                                                   int* scan, int* hist) {
   const int tid = threadIdx.x;
   // DynaExq hotness from the router trace: decayed count of routes per expert
@@ -325,57 +325,55 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
     hotness.hot[tid] = hotness.decay * hotness.hot[tid] + (float)(off[tid + 1] - off[tid]);
   const DevHandle& h = src.h;
   const bool active = src.active;
-  for (int gemm = 0; gemm < 2; ++gemm) {
-    const int bm = gemm == 0 ? bm13 : bm2;
-    TileEntry* tiles = gemm == 0 ? tiles13 : tiles2;
-    int32_t* ntiles = gemm == 0 ? ntiles13 : ntiles2;
-    const int ce = tid < E && active ? off[tid + 1] - off[tid] : 0;
-    auto put = [&](int at, int i, int rows) {
-      TileEntry te2;
-      te2.expert = tid;
-      te2.row_start = off[tid] + i * bm;
-      te2.rows = rows;
-      te2.tier = h.tier;
-      te2.w = gemm == 0 ? h.w13 : h.w2;
-      te2.pad = 0;
-      tiles[at] = te2;
-    };
-    if (bm < kSortTilesMinBm || bm > kMaxTileRows) {   // block-uniform
-      const int nt = (ce + bm - 1) / bm;
-      // one scan gives each expert's first tile (low 20 bits; a decode table
-      // holds far fewer than 2^20 tiles) and the number of experts spanning
-      // three or more tiles (high bits)
-      int tot = 0;
-      const int first = block_exclusive_scan(nt | (nt >= 3 ? 1 << 20 : 0), scan, tot) & 0xfffff;
-      for (int i = 0; i < nt; ++i) put(first + i, i, min(bm, ce - i * bm));
-      // ntiles[1]: some expert spans three or more tiles (the decode GEMMs
-      // then keep an expert's sub-tiles on one XCD)
-      if (tid == 0) {
-        ntiles[0] = tot & 0xfffff;
-        ntiles[1] = (tot >> 20) > 0 ? 1 : 0;
-      }
-    } else {
-      const int nfull = ce / bm, rem = ce - nfull * bm;
-      int nf = 0;
-      const int first = block_exclusive_scan(nfull, scan, nf);
-      for (int i = 0; i < nfull; ++i) put(first + i, i, bm);
-      const int key = bm - 1 - rem;                       // more rows first
-      if (tid < bm) hist[tid] = 0;
-      __syncthreads();
-      if (rem > 0) atomicAdd(&hist[key], 1);
-      __syncthreads();
-      const int cnt = tid < bm ? hist[tid] : 0;
-      int np = 0;
-      const int base = block_exclusive_scan(cnt, scan, np);   // its barriers order the read above
-      if (tid < bm) hist[tid] = base;
-      __syncthreads();
-      if (rem > 0) put(nf + atomicAdd(&hist[key], 1), nfull, rem);
-      if (tid == 0) {
-        ntiles[0] = nf + np;
-        ntiles[1] = 0;
-      }
-      __syncthreads();   // hist[] is reused by the next GEMM's table
-    }
+  // Both GEMMs use the same M-tiling: one pass places every tile and writes
+  // it to both tables, with the gate/up and the down weights.
+  const int ce = tid < E && active ? off[tid + 1] - off[tid] : 0;
+  auto put = [&](int at, int i, int rows) {
+    TileEntry te2;
+    te2.expert = tid;
+    te2.row_start = off[tid] + i * bm;
+    te2.rows = rows;
+    te2.tier = h.tier;
+    te2.pad = 0;
+    te2.w = h.w13;
+    tiles13[at] = te2;
+    te2.w = h.w2;
+    tiles2[at] = te2;
+  };
+  int count = 0, many = 0;
+  if (bm < kSortTilesMinBm || bm > kMaxTileRows) {   // block-uniform
+    const int nt = (ce + bm - 1) / bm;
+    // one scan gives each expert's first tile (low 20 bits; a decode table
+    // holds far fewer than 2^20 tiles) and the number of experts spanning
+    // three or more tiles (high bits)
+    int tot = 0;
+    const int first = block_exclusive_scan(nt | (nt >= 3 ? 1 << 20 : 0), scan, tot) & 0xfffff;
+    for (int i = 0; i < nt; ++i) put(first + i, i, min(bm, ce - i * bm));
+    count = tot & 0xfffff;
+    many = (tot >> 20) > 0 ? 1 : 0;
+  } else {
+    const int nfull = ce / bm, rem = ce - nfull * bm;
+    int nf = 0;
+    const int first = block_exclusive_scan(nfull, scan, nf);
+    for (int i = 0; i < nfull; ++i) put(first + i, i, bm);
+    const int key = bm - 1 - rem;                       // more rows first
+    if (tid < bm) hist[tid] = 0;
+    __syncthreads();
+    if (rem > 0) atomicAdd(&hist[key], 1);
+    __syncthreads();
+    const int cnt = tid < bm ? hist[tid] : 0;
+    int np = 0;
+    const int base = block_exclusive_scan(cnt, scan, np);   // its barriers order the read above
+    if (tid < bm) hist[tid] = base;
+    __syncthreads();
+    if (rem > 0) put(nf + atomicAdd(&hist[key], 1), nfull, rem);
+    count = nf + np;
+  }
+  // ntiles[1]: some expert spans three or more decode tiles (the decode
+  // GEMMs then keep an expert's sub-tiles on one XCD)
+  if (tid == 0) {
+    ntiles13[0] = ntiles2[0] = count;
+    ntiles13[1] = ntiles2[1] = many;
   }
 }
 
@@ -391,7 +389,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     const DevHandle* __restrict__ table, WaveMap wmap, Hotness hotness, const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
     int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
-    int32_t* __restrict__ ntiles2, int bm2) {
+    int32_t* __restrict__ ntiles2) {
   extern __shared__ int lds[];
   int* cnt = lds;                 // [16][E]
   int* off = cnt + 16 * E;        // [E+1] exclusive scan of totals
@@ -442,7 +440,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
   __syncthreads();
 
-  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan, hist);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, tiles2, ntiles2, bm13, scan, hist);
 }
 
 // Rank pass of the multi-block grouping (large T).  Block c owns the 256
@@ -491,7 +489,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
     const int32_t* __restrict__ rank, const int32_t* __restrict__ chunk_counts, int nchunks,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
     TileEntry* __restrict__ tiles13, int32_t* __restrict__ ntiles13, int bm13,
-    TileEntry* __restrict__ tiles2, int32_t* __restrict__ ntiles2, int bm2) {
+    TileEntry* __restrict__ tiles2, int32_t* __restrict__ ntiles2) {
   __shared__ int base[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int scan[16];
@@ -524,7 +522,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   }
   if (c != 0) return;
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
-  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan, hist);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, tiles2, ntiles2, bm13, scan, hist);
 }
 
 }  // namespace
@@ -594,6 +592,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
                           TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
                           int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,
                           hipStream_t s) {
+  if (bm13 != bm2) return hipErrorInvalidValue;   // the two GEMMs share one M-tiling
   if (T > kPermSmallT) {
     const int nchunks = (T + kPermChunk - 1) / kPermChunk;
     hipLaunchKernelGGL(permute_rank_kernel, dim3(nchunks), dim3(256), 0, s, ids, T, k, E, rank,
@@ -602,7 +601,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(1024), 0, s, table, wave, hotness, ids, T, k, E,
                        rank, chunk_counts, nchunks, offsets, sorted, pos, tiles13, ntiles13, bm13,
-                       tiles2, ntiles2, bm2);
+                       tiles2, ntiles2);
     return hipGetLastError();
   }
   const size_t lds = sizeof(int) * (17 * (size_t)E + 1025 + kMaxTileRows);
@@ -615,7 +614,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
     attr_set = true;
   }
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, wave, hotness, ids, T, k, E, offsets, sorted,
-                     pos, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2);
+                     pos, tiles13, ntiles13, bm13, tiles2, ntiles2);
   return hipGetLastError();
 }
 
