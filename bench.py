@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,11 +55,19 @@ def packed_bytes(tier, n, k):
     return 2 * n * k
 
 
+def _code_only(text: str) -> str:
+    """C/HIP source with comments removed and whitespace collapsed, so that
+    a comment edit does not change the hash of the code it describes."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(path_kind: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[path_kind]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -25,7 +25,8 @@
 // Packed layout: see quant_pack.hip.  A 16-byte load per lane of one 1 KB tile
 // gives that lane's B operands for four consecutive 32-wide MFMA k-steps of
 // one 16-column strip (int4), so B goes from HBM to registers with no LDS and
-// no cross-lane shuffles.  A (activations) is staged through LDS once.
+// no cross-lane shuffles.  A (activations) is staged through LDS, one K-chunk
+// at a time.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout used here: lane l holds row
 // (A) / column (B) l%16 and the 8 k-values 8*(l/16) .. +7 of the 32-wide step;
