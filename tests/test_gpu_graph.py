@@ -1,8 +1,10 @@
 """A captured forward replays correctly: several replays of a HIP graph holding
 one layer forward, with eager work and synchronizations in between, each give
-the eager result byte for byte: the decode path, the large-batch path with
-int4 and staged (int8/bf16) tiers, and at T = 2048 the MFMA router, the
-multi-block grouping and row-aware partial tiles."""
+the eager result byte for byte: the decode path (8-row tiles; split K at one
+token, with two strips per wave and K-chunks on the Mixtral shape; 16-row
+tiles in two K-chunks; the Zipf-skewed layer with its tiles grouped by XCD;
+at T = 2048 with the MFMA router, its group-sum pass and the multi-block
+grouping), and the large-batch path with int4 and staged (int8/bf16) tiers."""
 
 import numpy as np
 import pytest
@@ -12,7 +14,8 @@ from tests._harness import Setup, log
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cid,T", [(2, 32), (1, 64), (3, 512), (4, 2048)])
+@pytest.mark.parametrize("cid,T", [(2, 32), (1, 64), (3, 512), (4, 2048), (4, 1), (5, 1),
+                                   (6, 128), (3, 64)])
 def test_graph_replay_matches_eager(cid, T):
     import torch
     st = Setup(cid, T=T)
