@@ -134,26 +134,34 @@ __device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>:
 // s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // Rows of an M-tile in the decode kernel: ROWS = 8 (MFMA rows 8..15 are
-// copies) or 16 (all MFMA rows), chosen per forward from the mean rows per
-// expert.  Forwards take the decode kernels up to kDecodeRowsMax mean rows
+// copies), 16 (all MFMA rows) or 32 (two MFMA row blocks per weight load),
+// chosen per forward from the mean rows per expert.  Forwards take the decode kernels up to kDecodeRowsMax mean rows
 // per expert (kDecodeRowsMaxWide for layers with many experts, see
 // plan_gemm).
 constexpr int kDecodeTileGroup = 8;   // tiles per column block kept on one XCD (grouped mapping)
 constexpr int kDecodeRowsMax = 16;
 constexpr double kDecodeRowsMaxWide = 40.0;
-constexpr int kRStride = 16;     // group sums per k-group in LDS: all 16 MFMA rows
+// Group sums per k-group in LDS: one per MFMA row (16), or per tile row for
+// 32-row tiles (two 16-row MFMA blocks).
+__host__ __device__ constexpr int decode_rstride(int rows) { return rows > 16 ? rows : 16; }
 // A columns staged per chunk (multiples of kGroup): 4096 for 8-row tiles;
-// 1024 for 16-row tiles, so that a chunk stays near 33 KB of LDS and four
-// blocks fit a CU
+// 1024 for 16-row and 512 for 32-row tiles, so that a chunk stays near 33 KB
+// of LDS and four blocks fit a CU
+__host__ __device__ constexpr int decode_chunk_cap(int rows) {
+  return rows == 8 ? 4096 : rows == 16 ? 1024 : 512;
+}
 __host__ __device__ constexpr int decode_chunk_k(int K, int rows) {
-  return K < (rows == 8 ? 4096 : 1024) ? K : (rows == 8 ? 4096 : 1024);
+  return K < decode_chunk_cap(rows) ? K : decode_chunk_cap(rows);
 }
 
 template <int TIER, int NS, int WAVES, bool GATE_UP, bool KSPLIT, int ROWS>
 __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEntry& te,
                                                 const uint8_t* blob, int strip0, uint16_t* lds_a,
-                                                float* lds_r, f32x4_t (&acc)[NS]) {
+                                                float* lds_r,
+                                                f32x4_t (&acc)[(ROWS > 16 ? ROWS / 16 : 1) * NS]) {
   using TR = TierTraits<TIER>;
+  constexpr int RB = ROWS > 16 ? ROWS / 16 : 1;   // 16-row MFMA blocks per tile
+  constexpr int RS = decode_rstride(ROWS);
   const Int4Consts c4 = int4_consts();
   constexpr int D = TIER == MOE_TIER_INT4 ? 2 : 1;
   constexpr int L = TR::kLoads;
@@ -193,47 +201,54 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) row_scale[ns] = half_of(rs4, u0 + ns);
   }
-  // A fragments: lane l reads LDS row l % ROWS.  MFMA rows ROWS..15 (and rows
-  // at or beyond the tile's count) then hold copies or stale data; they only
-  // feed accumulator rows that the epilogue never stores, so no lane is masked.
-  const uint16_t* la = lds_a + (lane & (ROWS - 1)) * lda + 8 * (lane >> 4);
+  // A fragments: lane l reads LDS row l % ROWS (row 16 rb + l % 16 of MFMA
+  // block rb for 32-row tiles).  MFMA rows ROWS..15 (and rows at or beyond
+  // the tile's count) then hold copies or stale data; they only feed
+  // accumulator rows that the epilogue never stores, so no lane is masked.
+  const uint16_t* la = lds_a + (lane & ((ROWS > 16 ? 16 : ROWS) - 1)) * lda + 8 * (lane >> 4);
 
   // consume(g, d): k-group g (absolute), whose weights are in set d and whose
   // A columns and group sums sit at chunk-relative group g - c0 in LDS
   int c0 = 0;
   auto consume = [&](int g, int d) {
     const int gl = g - c0;
-    f32x4_t p[NS];
-    if constexpr (TIER == MOE_TIER_BF16) {
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) p[ns] = acc[ns];
-    } else {
-      const float4 r4 = *reinterpret_cast<const float4*>(lds_r + gl * kRStride + 4 * (lane >> 4));
-      const f32x4_t init = {-TR::kOffset * r4.x, -TR::kOffset * r4.y, -TR::kOffset * r4.z,
-                            -TR::kOffset * r4.w};
+    for (int rb = 0; rb < RB; ++rb) {   // 32-row tiles: both MFMA blocks take each weight load
+      f32x4_t p[NS];
+      if constexpr (TIER == MOE_TIER_BF16) {
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) p[ns] = init;
-    }
-    bf16x8_t af[4];
+        for (int ns = 0; ns < NS; ++ns) p[ns] = acc[rb * NS + ns];
+      } else {
+        const float4 r4 =
+            *reinterpret_cast<const float4*>(lds_r + gl * RS + 16 * rb + 4 * (lane >> 4));
+        const f32x4_t init = {-TR::kOffset * r4.x, -TR::kOffset * r4.y, -TR::kOffset * r4.z,
+                              -TR::kOffset * r4.w};
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) af[s4] = as_bf16x8(load_u32x4(la + kGroup * gl + 32 * s4));
+        for (int ns = 0; ns < NS; ++ns) p[ns] = init;
+      }
+      bf16x8_t af[4];
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
+      for (int s4 = 0; s4 < 4; ++s4)
+        af[s4] = as_bf16x8(load_u32x4(la + 16 * rb * lda + kGroup * gl + 32 * s4));
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) p[ns] = mfma16x16x32(af[s4], b_operand<TIER>(bb[d][ns], s4, c4), p[ns]);
-    if constexpr (TIER == MOE_TIER_BF16) {
+      for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) acc[ns] = p[ns];
-    } else {
+        for (int s4 = 0; s4 < 4; ++s4) p[ns] = mfma16x16x32(af[s4], b_operand<TIER>(bb[d][ns], s4, c4), p[ns]);
+      if constexpr (TIER == MOE_TIER_BF16) {
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        float scf;
-        if constexpr (TIER == MOE_TIER_INT4)
-          scf = half_of(sc[d], ns);
-        else
-          scf = row_scale[ns];
+        for (int ns = 0; ns < NS; ++ns) acc[rb * NS + ns] = p[ns];
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(scf, p[ns][i], acc[ns][i]);
+        for (int ns = 0; ns < NS; ++ns) {
+          float scf;
+          if constexpr (TIER == MOE_TIER_INT4)
+            scf = half_of(sc[d], ns);
+          else
+            scf = row_scale[ns];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[rb * NS + ns][i] = __builtin_fmaf(scf, p[ns][i], acc[rb * NS + ns][i]);
+        }
       }
     }
   };
@@ -269,8 +284,8 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
         *reinterpret_cast<uint4*>(lds_a + m * lda + col) = *reinterpret_cast<const uint4*>(src);
       }
       if constexpr (TIER != MOE_TIER_BF16) {
-        for (int i = threadIdx.x; i < (ce - cs) * kRStride; i += 64 * WAVES) {
-          const int gl = i / kRStride, m = i - gl * kRStride;
+        for (int i = threadIdx.x; i < (ce - cs) * RS; i += 64 * WAVES) {
+          const int gl = i / RS, m = i - gl * RS;
           float r = 0.0f;
           if (m < rows) {
             const int pos = te.row_start + m;
@@ -321,12 +336,14 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 
 // Occupancy: three waves per SIMD for gate/up (K = H, long weight streams);
 // four for down, whose short K (I) makes more, shorter waves, all of which
-// then fit in one round at the decode workloads.
+// then fit in one round at the decode workloads.  32-row tiles hold two
+// accumulator blocks per strip: two waves per SIMD.
 // KSPLIT (few tiles, so few waves for the GPU): the block's waves share its
 // NS strips and split every staged K-chunk; their partial sums meet in LDS,
 // added in wave order, and wave 0 runs the epilogue.
 template <int NS, int WAVES, bool GATE_UP, bool KSPLIT, int ROWS>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(GATE_UP ? 3 : 4, GATE_UP ? 3 : 4)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(
+    ROWS > 16 ? 2 : (GATE_UP ? 3 : 4), ROWS > 16 ? 2 : (GATE_UP ? 3 : 4))))
 void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   static_assert(!GATE_UP || NS == 4, "a gate/up wave covers 32 gate + 32 up columns");
   static_assert(NS == 1 || NS == 2 || NS == 4, "a wave's strips lie in one quad");
@@ -365,12 +382,13 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const int chunk = KSPLIT ? nb : nb * WAVES + wave;   // this wave's group of NS strips
   const int strip0 = chunk * NS;
   uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
-  static_assert(ROWS == 8 || ROWS == 16, "an M-tile is 8 or 16 rows");
+  static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "an M-tile is 8, 16 or 32 rows");
+  constexpr int RB = ROWS > 16 ? ROWS / 16 : 1;   // 16-row MFMA blocks per tile
   float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)ROWS * (decode_chunk_k(a.K, ROWS) + 8) * 2);
 
-  f32x4_t acc[NS];
+  f32x4_t acc[RB * NS];
 #pragma unroll
-  for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < RB * NS; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint8_t* blob = te.w;
   switch (te.tier) {
     case MOE_TIER_INT4:
@@ -385,67 +403,74 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   }
   if constexpr (KSPLIT) {
     static_assert(WAVES >= 2, "a split needs several waves");
-    float* red = reinterpret_cast<float*>(dyn_lds);   // [WAVES - 1][NS * 4][64]
+    float* red = reinterpret_cast<float*>(dyn_lds);   // [WAVES - 1][RB * NS * 4][64]
     __syncthreads();                                  // every wave is done with A in LDS
     if (wave > 0) {
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
+      for (int q = 0; q < RB * NS; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[((wave - 1) * NS * 4 + ns * 4 + i) * 64 + lane] = acc[ns][i];
+        for (int i = 0; i < 4; ++i) red[((wave - 1) * RB * NS * 4 + q * 4 + i) * 64 + lane] = acc[q][i];
     }
     __syncthreads();
     if (wave > 0) return;
     for (int w = 1; w < WAVES; ++w)
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
+      for (int q = 0; q < RB * NS; ++q)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[ns][i] += red[((w - 1) * NS * 4 + ns * 4 + i) * 64 + lane];
+        for (int i = 0; i < 4; ++i) acc[q][i] += red[((w - 1) * RB * NS * 4 + q * 4 + i) * 64 + lane];
   }
 
   if constexpr (GATE_UP) {
     // SwiGLU on strips (0,2) and (1,3): gate and up of 32 activation columns
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int icol = 32 * chunk + 16 * half + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * (lane >> 4) + i;
-        const uint32_t a16 = f32_to_bf16_rne(silu_f32(acc[half][i]) * acc[half + 2][i]);
-        if (m < te.rows) {
-          a.act[(size_t)(te.row_start + m) * a.I + icol] = (uint16_t)a16;
-          rs[i] += bf16_to_f32(a16);
-        }
-      }
-    }
     const int P = a.I / 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = rs[i];
+    for (int rb = 0; rb < RB; ++rb) {
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
-      const int m = 4 * (lane >> 4) + i;
-      if ((lane & 15) == 0 && m < te.rows) a.r2[(size_t)(te.row_start + m) * P + chunk] = v;
+      for (int half = 0; half < 2; ++half) {
+        const int icol = 32 * chunk + 16 * half + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * rb + 4 * (lane >> 4) + i;
+          const uint32_t a16 =
+              f32_to_bf16_rne(silu_f32(acc[rb * NS + half][i]) * acc[rb * NS + half + 2][i]);
+          if (m < te.rows) {
+            a.act[(size_t)(te.row_start + m) * a.I + icol] = (uint16_t)a16;
+            rs[i] += bf16_to_f32(a16);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = rs[i];
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 16);
+        const int m = 16 * rb + 4 * (lane >> 4) + i;
+        if ((lane & 15) == 0 && m < te.rows) a.r2[(size_t)(te.row_start + m) * P + chunk] = v;
+      }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * (lane >> 4) + i;
-      if (m < te.rows) {
-        const int pos = te.row_start + m;
-        const float wgt = a.topk_w[a.sorted[pos]];
-        float* out = a.rows + (size_t)pos * a.N + 16 * strip0 + (lane & 15);
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) out[16 * ns] = wgt * acc[ns][i];
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * rb + 4 * (lane >> 4) + i;
+        if (m < te.rows) {
+          const int pos = te.row_start + m;
+          const float wgt = a.topk_w[a.sorted[pos]];
+          float* out = a.rows + (size_t)pos * a.N + 16 * strip0 + (lane & 15);
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) out[16 * ns] = wgt * acc[rb * NS + ns][i];
+        }
       }
-    }
   }
 }
 
 size_t decode_lds_bytes(int K, int rows, int NS, int WAVES, bool ksplit) {
   const int KC = decode_chunk_k(K, rows);
-  const size_t stage = (size_t)rows * (KC + 8) * 2 + (size_t)(KC / kGroup) * kRStride * 4;
-  const size_t red = ksplit ? (size_t)(WAVES - 1) * NS * 4 * 64 * 4 : 0;
+  const size_t stage = (size_t)rows * (KC + 8) * 2 + (size_t)(KC / kGroup) * decode_rstride(rows) * 4;
+  const int rb = rows > 16 ? rows / 16 : 1;
+  const size_t red = ksplit ? (size_t)(WAVES - 1) * rb * NS * 4 * 64 * 4 : 0;
   return stage > red ? stage : red;
 }
 
@@ -491,8 +516,10 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
   };
   using R8 = std::integral_constant<int, 8>;
   using R16 = std::integral_constant<int, 16>;
+  using R32 = std::integral_constant<int, 32>;
   if (rows == 8) return ksplit ? run(std::true_type{}, R8{}) : run(std::false_type{}, R8{});
   if (rows == 16) return ksplit ? run(std::true_type{}, R16{}) : run(std::false_type{}, R16{});
+  if (rows == 32) return ksplit ? run(std::true_type{}, R32{}) : run(std::false_type{}, R32{});
   return hipErrorInvalidValue;
 }
 
@@ -553,6 +580,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }  // namespace
 
 constexpr double kDecodeRows8Max = 4.0;   // mean rows per expert up to which tiles are 8 rows
+constexpr double kDecodeRows32Min = 12.0, kDecodeRows32Max = 24.0;   // 32-row tiles in (min, max]
 
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
@@ -569,8 +597,22 @@ GemmPlan plan_gemm(const Layer& L, int T) {
   const bool decode = rows_per_expert <= decode_max;
   p.kind = decode ? kGemmDecode : kGemmPrefill;
   // 8-row tiles while few experts overflow them (the LDS staging then fits
-  // any K up to 4096 in one chunk); 16-row tiles above
-  p.bm13 = decode ? (rows_per_expert <= kDecodeRows8Max ? 8 : 16) : 256;
+  // any K up to 4096 in one chunk); 16-row tiles above; 32-row tiles (two
+  // waves per SIMD) between 12 and 24 mean rows, where they stream most
+  // experts' weights once instead of twice: Mixtral T = 64 277 -> 259 us,
+  // Qwen3-80B T = 1024 397 -> 371 us, Zipf-biased Qwen3-30B T = 256 206 ->
+  // 183 us.  At 40 rows (Qwen3-80B T = 2048) they were 4% slower than 16-row
+  // tiles, on the OLMoE shape at 16 rows 2% slower, and with the few tiles
+  // of a split-K launch (the tiny layer) 12% slower, so not there.
+  int bm = 256;
+  if (decode) {
+    const long tiles = std::min<long>(L.E, (long)T * L.k);
+    const bool wide = tiles * (2L * L.I / 64) >= kDecodeSplitWaves;   // gate/up not split-K
+    bm = rows_per_expert <= kDecodeRows8Max ? 8
+         : (wide && rows_per_expert > kDecodeRows32Min && rows_per_expert <= kDecodeRows32Max) ? 32
+         : 16;
+  }
+  p.bm13 = bm;
   p.bm2 = p.bm13;
   return p;
 }

@@ -91,12 +91,14 @@ def test_layer_mixtral_prefill_sampled():
     _run(st, subset=sub, keep=False, runs=2)
 
 
-@pytest.mark.parametrize("T", [1, 32])
+@pytest.mark.parametrize("T", [1, 32, 64])
 def test_layer_mixtral_decode_sampled(T):
     """Mixtral shape at decode sizes: the down GEMM's K = 14336 is staged in
-    four K-chunks (the last one partial), gate/up's K = 4096 in one."""
+    K-chunks: four with 8-row tiles at T = 1 (the last one partial),
+    fourteen with 16-row tiles at T = 32, twenty-eight with 32-row tiles at
+    T = 64."""
     st = Setup(5, T=T)
-    sub = [0] if T == 1 else [0, 31]
+    sub = [0] if T == 1 else [0, T - 1]
     _run(st, subset=sub, keep=False, runs=2)
 
 
