@@ -144,6 +144,26 @@ def test_k_equals_e_and_single_expert():
     _run(Setup(1, T=24, cfg=c1))
 
 
+def test_max_experts_and_top_k():
+    """The library's limits: 1024 experts (one grouping thread each, 16
+    expert slots per top-k lane) and top-16 routing, on a small hidden size;
+    routing bit-exact and the layer within the gate."""
+    import torch
+    c = dataclasses.replace(inputs.get_config(1), hidden=256, inter=128, n_experts=1024,
+                            top_k=16, max_tokens=40)
+    st = Setup(1, T=40, cfg=c)
+    layer = st.gpu_layer()
+    x, wr, b = st.dev_inputs()
+    got = {k: v.cpu().numpy() for k, v in layer.route(x, wr, b).items()}
+    torch.cuda.synchronize()
+    ref = oracle.route(st.x, st.wr, st.bias, st.k)
+    assert np.array_equal(got["logits"].view(np.uint32), ref["logits"].view(np.uint32))
+    for key in ("ids", "offsets", "sorted_routes", "route_pos"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert np.max(np.abs(got["weights"] - ref["weights"])) <= 1e-6
+    _run(st, layer=layer, keep=False)
+
+
 def test_zero_tokens():
     import torch
     st = Setup(1, T=1)
