@@ -523,9 +523,12 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
   return hipErrorInvalidValue;
 }
 
+// Decode tiles a forward is expected to have: one per touched expert, at
+// most min(E, T k) (the launch heuristics below; the grid uses the bound).
+long est_decode_tiles(const Layer& L, int T) { return std::min<long>(L.E, (long)T * L.k); }
+
 bool decode_split_k(const Layer& L, int T, int N) {
-  const long tiles = std::min<long>(L.E, (long)T * L.k);
-  return tiles * (N / 64) < kDecodeSplitWaves;
+  return est_decode_tiles(L, T) * (N / 64) < kDecodeSplitWaves;
 }
 
 
@@ -606,8 +609,7 @@ GemmPlan plan_gemm(const Layer& L, int T) {
   // of a split-K launch (the tiny layer) 12% slower, so not there.
   int bm = 256;
   if (decode) {
-    const long tiles = std::min<long>(L.E, (long)T * L.k);
-    const bool wide = tiles * (2L * L.I / 64) >= kDecodeSplitWaves;   // gate/up not split-K
+    const bool wide = !decode_split_k(L, T, 2 * L.I);   // the gate/up launch is not split-K
     bm = rows_per_expert <= kDecodeRows8Max ? 8
          : (wide && rows_per_expert > kDecodeRows32Min && rows_per_expert <= kDecodeRows32Max) ? 32
          : 16;
@@ -658,8 +660,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   // over one or two tiles, e.g. the Mixtral shape at one token): two strips
   // per wave double the blocks.  Mixtral T = 1: 64.9 -> 61.3 us per layer;
   // at 1280 or more waves it gained nothing, and at T = 4 it lost 7%.
-  const long est_tiles = std::min<long>(L.E, (long)T * L.k);
-  if (ks && est_tiles * (a.N / 64) * 4 < kDecodeSplitWaves)
+  if (ks && est_decode_tiles(L, T) * (a.N / 64) * 4 < kDecodeSplitWaves)
     return launch_decode<2, false>(a, max_tiles, gp.bm2, ks, s, KernelTimer{nullptr, nullptr});
   return launch_decode<4, false>(a, max_tiles, gp.bm2, ks, s, KernelTimer{nullptr, nullptr});
 }
