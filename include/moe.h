@@ -240,7 +240,10 @@ size_t moe_workspace_size(moe_layer_t layer, int32_t T);
  * by default when T >= 256, E >= 32 and T*E*H >= 2^29): approximate logits on
  * bf16 MFMA and an error bound against this fixed order leave a few candidate
  * experts per token, whose logits are then summed in the fixed order; the
- * results are the same bit for bit.
+ * results are the same bit for bit.  With logits NULL, T <= 64, E <= 128 and
+ * at most 256 KiB of router weights, one launch computes each token's
+ * logits in this fixed order on chip and takes its top k there (again the
+ * same results).
  * T may be 0 (then only expert_offsets is written, all zero). */
 int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
               const float* bias, int32_t T, int32_t* topk_ids, float* topk_w,
