@@ -104,7 +104,8 @@ typedef struct moe_expert_handle {
 } moe_expert_handle;
 
 /* Layer geometry.  Constraints: hidden % 256 == 0, inter % 128 == 0,
- * 1 <= n_experts <= 1024, 1 <= top_k <= min(n_experts, 16). */
+ * 1 <= n_experts <= 1024, 1 <= top_k <= min(n_experts, 16), and an expert's
+ * bf16 gate/up matrix (2 * inter * hidden * 2 bytes) below 4 GiB. */
 typedef struct moe_layer_desc {
   int32_t hidden;     /* H */
   int32_t inter;      /* I (per-expert intermediate size) */
@@ -120,6 +121,24 @@ typedef struct moe_layer_s* moe_layer_t;
  * Returns 0 for a bad tier or a shape the layout cannot hold
  * (k_in % 128 != 0 or n_out % 64 != 0). */
 size_t moe_packed_size(int tier, int64_t n_out, int64_t k_in);
+
+/* Read a packed blob back into row-major codes and scales, on the host (no
+ * GPU work; the inverse of the layout moe_quantize_pack writes).  ExactMoE
+ * §3.3: packed gate/up codes, packed down codes and FP16 scales in the
+ * kernel's own format; this makes that format checkable against the §3.2
+ * quantizer without a GPU.
+ *   src, src_bytes  host copy of the blob (at least the payload:
+ *                   moe_packed_size without its padding).
+ *   layout          the layout it was packed with; rows come back in source
+ *                   order (gate rows 0..I-1, then up rows, for MOE_LAYOUT_GATE_UP).
+ *   q    host int8 [n_out, k_in]: the codes q (int4: -8..7, int8: -128..127);
+ *        unused (may be NULL) for MOE_TIER_BF16.
+ *   aux  host uint16: int4 the fp16 scale bits [n_out, k_in/128]; int8 the fp16
+ *        row scales [n_out]; bf16 the weights' bf16 bits [n_out, k_in].
+ * MOE_EINVAL for a bad tier, layout or null pointer, MOE_ESHAPE for a shape the
+ * layout cannot hold, MOE_ENOSPC if src_bytes is below the payload. */
+int moe_unpack_codes(int tier, int layout, const void* src, size_t src_bytes, int64_t n_out,
+                     int64_t k_in, int8_t* q, uint16_t* aux);
 
 /* Quantize (ExactMoE §3.2; int8: the same rule per row with range +-127) and
  * pack one matrix into the kernel's layout, on the GPU.
@@ -218,6 +237,17 @@ int moe_layer_set_router_mode(moe_layer_t layer, int32_t mode);
  * stream that has work using the layer. */
 int moe_layer_destroy(moe_layer_t layer);
 
+/* Which grouped-GEMM family and M-tile height a forward of T tokens takes
+ * (a diagnostic for callers and tests; it never changes results).
+ *   path       1: few routes per expert (weight streaming, exact integer MFMA
+ *              operands); 2: many routes per expert (fp16 MFMA, dequantized
+ *              weights rounded once to fp16).
+ *   tile_rows  routes per M-tile of both grouped GEMMs: an expert's routes, in
+ *              grouped order, are cut into tiles of this many (the last one
+ *              ragged).
+ * Host only; MOE_EINVAL for null pointers, MOE_ESHAPE for T outside [0, 2^24]. */
+int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_rows);
+
 /* Bytes of device workspace a route or forward call with T tokens needs.
  * The workspace is scratch: no state is kept in it between calls, except that
  * a moe_layer_forward_wave with accumulate = 1 reads the routing left by the
@@ -257,7 +287,11 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
  *   ws: device workspace of ws_bytes >= moe_workspace_size(layer, T), 256-byte
  *     aligned.  x and y must be 16-byte aligned.
  * T may be 0 (nothing is enqueued).  Calls that share a workspace must be
- * ordered on one stream. */
+ * ordered on one stream.
+ * When a call takes the many-routes-per-expert path (moe_layer_plan path 2),
+ * T*H*2 and T*k*I*2 must each stay below 4 GiB (its kernels address these
+ * 16-bit activation arrays with 32-bit offsets): MOE_ESHAPE otherwise, before
+ * any work is enqueued; split such a batch into several calls. */
 int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
                       const float* bias, int32_t T, void* y, int y_dtype, void* ws,
                       size_t ws_bytes, void* stream);

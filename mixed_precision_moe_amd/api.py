@@ -120,6 +120,11 @@ class Layer:
         self._h = out
         self._events = None
         self._ws: Dict[Tuple[int, int], torch.Tensor] = {}
+        # waves keep their own workspaces (an accumulating wave reads the
+        # routing its layer call's first wave left there) and remember which
+        # of them hold such a first wave
+        self._wave_ws: Dict[Tuple[int, int], torch.Tensor] = {}
+        self._wave_routed: set = set()
 
     @staticmethod
     def _handle_array(handles):
@@ -139,6 +144,14 @@ class Layer:
 
     def workspace_size(self, T: int) -> int:
         return int(self._lib.moe_workspace_size(self._h, int(T)))
+
+    def plan(self, T: int) -> Tuple[int, int]:
+        """(path, tile_rows) a forward of T tokens takes: path 1 = few routes
+        per expert (weight streaming), 2 = many (fp16 MFMA); routes per M-tile."""
+        path, rows = ctypes.c_int32(), ctypes.c_int32()
+        check(self._lib.moe_layer_plan(self._h, int(T), ctypes.byref(path), ctypes.byref(rows)),
+              "moe_layer_plan")
+        return path.value, rows.value
 
     def workspace(self, T: int, device) -> torch.Tensor:
         """A cached workspace tensor large enough for T tokens (allocated by torch)."""
@@ -251,8 +264,12 @@ class Layer:
                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         """One wave over the experts the current slot map sends to slots
         (y = or y += the wave's output; accumulating needs an fp32 y and reuses
-        the routing the previous wave left in the workspace, so without an
-        explicit workspace the layer keeps one per token count for its waves)."""
+        the routing the previous wave left in the workspace).  Without an
+        explicit workspace the layer keeps one per token count for its waves,
+        apart from the one forward() and route() use, and refuses an
+        accumulating wave that no first wave (accumulate=False) of the same
+        token count has routed since the last set_router_mode.  With an
+        explicit workspace that ordering is the caller's to keep."""
         _require_cuda(x, "x", _BF16)
         _require_cuda(wr, "wr", _BF16)
         if bias is not None:
@@ -263,16 +280,21 @@ class Layer:
         _require_cuda(y, "y", (torch.float32, torch.bfloat16))
         yd = DTYPE_F32 if y.dtype == torch.float32 else DTYPE_BF16
         if workspace is None:
-            cache = self.__dict__.setdefault("_wave_ws", {})
-            key = (T, str(x.device))
-            if key not in cache:
-                cache[key] = self.workspace(T, x.device)
-            ws = cache[key]
+            key = (x.device.index or 0, int(T))
+            if accumulate and key not in self._wave_routed:
+                raise ValueError("an accumulating wave needs a first wave (accumulate=False) of the "
+                                 "same token count, after the last set_router_mode")
+            ws = self._wave_ws.get(key)
+            if ws is None:
+                ws = torch.empty(max(256, self.workspace_size(T)), dtype=torch.uint8, device=x.device)
+                self._wave_ws[key] = ws
         else:
             ws = workspace
         check(self._lib.moe_layer_forward_wave(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias), T,
                                                y.data_ptr(), yd, int(bool(accumulate)), ws.data_ptr(),
                                                ws.numel(), _stream(stream)), "moe_layer_forward_wave")
+        if workspace is None and not accumulate:
+            self._wave_routed.add((x.device.index or 0, int(T)))
         return y
 
     def set_stage_events(self, events: Optional[Sequence["torch.cuda.Event"]]) -> None:
@@ -295,7 +317,8 @@ class Layer:
         workspaces are dropped)."""
         check(self._lib.moe_layer_set_router_mode(self._h, int(mode)), "set_router_mode")
         self._ws.clear()
-        self.__dict__.pop("_wave_ws", None)
+        self._wave_ws.clear()
+        self._wave_routed.clear()
 
     def close(self) -> None:
         if getattr(self, "_h", None):

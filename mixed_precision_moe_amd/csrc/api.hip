@@ -27,6 +27,8 @@ int set_error(int status, const char* fmt, ...) {
   return status;
 }
 
+void clear_error() { g_err[0] = 0; }
+
 int check_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return MOE_OK;
   return set_error(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -59,6 +61,7 @@ WsPlan plan_workspace(const Layer& L, int T, const GemmPlan& gp) {
   w.pos = take(sizeof(int32_t) * R);
   w.rank = take(sizeof(int32_t) * R);
   w.chunk_counts = take(sizeof(int32_t) * (size_t)((T + kPermChunk - 1) / kPermChunk) * L.E);
+  w.chunk_tot = take(sizeof(int32_t) * (size_t)L.E);
   w.xn2 = take(sizeof(float) * (size_t)T * S);
   w.wn2 = take(sizeof(float) * (size_t)L.E * S);
   w.tiles13 = take(sizeof(TileEntry) * (size_t)(w.max_tiles13 > 0 ? w.max_tiles13 : 1));
@@ -264,6 +267,11 @@ int moe_layer_create(const moe_layer_desc* d, const moe_expert_handle* table, vo
   if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->n_experts)
     return set_error(MOE_ESHAPE, "top_k must be in [1, min(n_experts, %d)] (got %d)", kMaxTopK,
                      d->top_k);
+  // the GEMMs address an expert's blob through 32-bit buffer records: the
+  // largest tier (bf16) of the gate/up matrix must stay below 4 GiB
+  if ((uint64_t)2 * d->inter * 2 * (uint64_t)d->hidden > 0xffffffffull)
+    return set_error(MOE_ESHAPE, "an expert's bf16 gate/up matrix (2 x %d x %d x 2 bytes) must stay below 4 GiB",
+                     d->inter, d->hidden);
   int rc = validate_handles(table, d->n_experts);
   if (rc) return rc;
   Layer* L = new (std::nothrow) Layer();
@@ -413,6 +421,17 @@ int moe_layer_destroy(moe_layer_t layer) {
   return rc ? rc : rc2 ? rc2 : rc3;
 }
 
+int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_rows) {
+  g_err[0] = 0;
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  if (!L || !path || !tile_rows) return set_error(MOE_EINVAL, "null pointer");
+  if (T < 0 || T > (1 << 24)) return set_error(MOE_ESHAPE, "bad token count %d", T);
+  const GemmPlan gp = plan_gemm(*L, T);
+  *path = gp.kind;
+  *tile_rows = gp.bm13;
+  return MOE_OK;
+}
+
 size_t moe_workspace_size(moe_layer_t layer, int32_t T) {
   const Layer* L = reinterpret_cast<const Layer*>(layer);
   if (!L || T < 0) return 0;
@@ -448,8 +467,9 @@ int moe_layer_set_router_mode(moe_layer_t layer, int32_t mode) {
 
 namespace {
 
+// gemm: the call runs the grouped GEMMs (a forward), not only the routing.
 int check_common(const Layer* L, const uint16_t* x, const uint16_t* wr, int32_t T, void* ws,
-                 size_t ws_bytes, WsPlan* plan, GemmPlan* gp) {
+                 size_t ws_bytes, WsPlan* plan, GemmPlan* gp, bool gemm) {
   if (!L) return set_error(MOE_EINVAL, "null layer");
   if (T < 0 || T > (1 << 24)) return set_error(MOE_ESHAPE, "bad token count %d", T);
   if ((size_t)T * L->k > (size_t)1 << 28) return set_error(MOE_ESHAPE, "too many routes");
@@ -459,6 +479,15 @@ int check_common(const Layer* L, const uint16_t* x, const uint16_t* wr, int32_t 
   if (T > 0 && !aligned(ws, kBlobAlign))
     return set_error(MOE_EINVAL, "workspace must be 256-byte aligned");
   *gp = plan_gemm(*L, T);
+  // The large-batch GEMMs read their 16-bit activations (x [T, H] and the
+  // SwiGLU output [T k, I]) through 32-bit buffer records and offsets, so each
+  // array must stay below 4 GiB; larger batches are split by the caller.
+  if (gemm && gp->kind == kGemmPrefill &&
+      ((uint64_t)T * L->H * 2 > 0xffffffffull || (uint64_t)T * L->k * L->I * 2 > 0xffffffffull))
+    return set_error(MOE_ESHAPE,
+                     "%d tokens: the large-batch path needs T*H*2 and T*k*I*2 below 4 GiB "
+                     "(H %d, k %d, I %d); split the batch",
+                     T, L->H, L->k, L->I);
   *plan = plan_workspace(*L, T, *gp);
   if (T > 0 && ws_bytes < plan->total)
     return set_error(MOE_ENOSPC, "workspace has %zu bytes, %zu needed", ws_bytes, plan->total);
@@ -525,7 +554,7 @@ hipError_t enqueue_route(const Layer& L, WaveMap wave, Hotness hotness, const Ws
   return launch_permute(L.table, wave, hotness, ids, T, L.k, L.E, offsets, sorted, pos, at<TileEntry>(ws, p.tiles13),
                         at<int32_t>(ws, p.ntiles13), gp.bm13, at<TileEntry>(ws, p.tiles2),
                         at<int32_t>(ws, p.ntiles2), gp.bm2, at<int32_t>(ws, p.rank),
-                        at<int32_t>(ws, p.chunk_counts), st.s);
+                        at<int32_t>(ws, p.chunk_counts), at<int32_t>(ws, p.chunk_tot), st.s);
 }
 
 }  // namespace
@@ -537,7 +566,7 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
                         void* ws, size_t ws_bytes, void* stream) {
   WsPlan p;
   GemmPlan gp;
-  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
+  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp, true);
   if (rc) return rc;
   if (y_dtype != MOE_DTYPE_BF16 && y_dtype != MOE_DTYPE_F32)
     return set_error(MOE_EINVAL, "bad y_dtype %d", y_dtype);
@@ -602,7 +631,7 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const fl
   const Layer* L = reinterpret_cast<const Layer*>(layer);
   WsPlan p;
   GemmPlan gp;
-  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp);
+  int rc = check_common(L, x, wr, T, ws, ws_bytes, &p, &gp, false);
   if (rc) return rc;
   if (!expert_offsets || (T > 0 && (!topk_ids || !topk_w || !sorted_routes || !route_pos)))
     return set_error(MOE_EINVAL, "null output pointer");

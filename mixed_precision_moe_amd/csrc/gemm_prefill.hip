@@ -629,15 +629,11 @@ hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a
   a.I = L.I;
   a.topk_w = topk_w;
   a.rows = rows;
-  static bool attr[2] = {false, false};
+  static DeviceOnce lds_opt_in[2];
   const void* kern = gate_up ? reinterpret_cast<const void*>(gemm_prefill_kernel<true>)
                              : reinterpret_cast<const void*>(gemm_prefill_kernel<false>);
-  if (!attr[gate_up]) {
-    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)kPrefillLds);
-    if (e != hipSuccess) return e;
-    attr[gate_up] = true;
-  }
+  const hipError_t ea = ensure_dynamic_lds(lds_opt_in[gate_up ? 1 : 0], kern, (int)kPrefillLds);
+  if (ea != hipSuccess) return ea;
   // Down GEMM with a long K (= I): an M-tile's column blocks share one XCD,
   // whose L2 then takes the tile's activation rows (256 x I fp16) once
   // instead of in every XCD: 3.5% faster on the Mixtral shape (I 14336).

@@ -493,13 +493,9 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
     constexpr bool KS = decltype(split_c)::value;
     constexpr int RW = decltype(rows_c)::value;
     auto kern = gemm_decode_kernel<NS, W, GATE_UP, KS, RW>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static DeviceOnce lds_opt_in;   // one per instantiation
+    const hipError_t ea = ensure_dynamic_lds(lds_opt_in, reinterpret_cast<const void*>(kern), 160 * 1024);
+    if (ea != hipSuccess) return ea;
     const int bpt = KS ? chunks : chunks / W;
     unsigned blocks = (unsigned)(max_tiles * bpt);
     if (a.tile_group) {   // whole groups of Q tiles, then whole rounds of 8 groups

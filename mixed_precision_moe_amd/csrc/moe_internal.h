@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe.h"
 
 namespace moe {
@@ -77,7 +79,7 @@ struct GemmPlan {
 // Byte offsets of the workspace regions for T tokens.
 struct WsPlan {
   size_t logits, ids, weights, offsets, sorted, pos, tiles13, ntiles13, tiles2, ntiles2;
-  size_t rank, chunk_counts, xn2, wn2;
+  size_t rank, chunk_counts, chunk_tot, xn2, wn2;
   size_t r13, act, r2, rows, x16;
   size_t total;
   int max_tiles13, max_tiles2;
@@ -124,6 +126,25 @@ struct Hotness {
 // error state ---------------------------------------------------------------
 int set_error(int status, const char* fmt, ...);
 int check_hip(hipError_t e, const char* what);
+void clear_error();
+
+// Kernels that take more than 64 KB of dynamic LDS need an opt-in per kernel
+// and device (hipFuncSetAttribute acts on the current device).  One bit per
+// device records that it was made; concurrent first calls may both set it,
+// which is harmless.
+struct DeviceOnce {
+  std::atomic<uint64_t> done{0};
+};
+inline hipError_t ensure_dynamic_lds(DeviceOnce& once, const void* kern, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (once.done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) once.done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // planning ------------------------------------------------------------------
 GemmPlan plan_gemm(const Layer& L, int T);
@@ -164,14 +185,15 @@ bool use_small_router(int T, int E, int H);
 hipError_t launch_router_topk_small(const uint16_t* x, const uint16_t* wr, const float* bias,
                                     int T, int H, int E, int k, float* r13, int32_t* ids,
                                     float* w, hipStream_t s);
-// Grouping: one workgroup for T <= kPermSmallT, else a rank pass and a
-// scatter pass over blocks of kPermChunk tokens (rank [T*k] and chunk_counts
-// [ceil(T / kPermChunk) * E] are workspace).
+// Grouping: one workgroup for T <= kPermSmallT, else a rank pass, a
+// per-expert scan over the token blocks and a scatter pass, over blocks of
+// kPermChunk tokens (rank [T*k], chunk_counts [ceil(T / kPermChunk) * E] and
+// chunk_tot [E] are workspace).
 hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness, const int32_t* ids, int T, int k,
                           int E, int32_t* offsets, int32_t* sorted, int32_t* pos,
                           TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
                           int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,
-                          hipStream_t s);
+                          int32_t* chunk_tot, hipStream_t s);
 hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16_t* x,
                          const int32_t* sorted, const TileEntry* tiles, const int32_t* ntiles,
                          int max_tiles, const float* r13, uint16_t* act, float* r2,

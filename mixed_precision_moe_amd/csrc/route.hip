@@ -479,17 +479,49 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
     chunk_counts[(size_t)blockIdx.x * E + e] = cnt[0][e] + cnt[1][e] + cnt[2][e] + cnt[3][e];
 }
 
-// Scatter pass of the multi-block grouping.  Block c sums the per-block
-// counts into its bases (routes of each expert in blocks before c) and the
-// totals, scans the totals into the expert offsets, and places its routes at
-// offset + base + rank: the stable order by (expert, token).  Block 0 also
-// writes the offsets and the M-tile tables.
+// Scan pass of the multi-block grouping: per expert e (one thread each),
+// chunk_counts[c][e] becomes the number of routes to e in token blocks before
+// c (exclusive prefix over c, in place) and chunk_tot[e] the total.  Every
+// count is read once, so the pass costs O(nchunks * E) for any T; the loads of
+// eight blocks are issued before their adds.
+__global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ chunk_counts,
+                                                           int32_t* __restrict__ chunk_tot,
+                                                           int nchunks, int E) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  int32_t* col = chunk_counts + e;
+  int run = 0;
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = col[(size_t)(c + i) * E];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      col[(size_t)(c + i) * E] = run;
+      run += v[i];
+    }
+  }
+  for (; c < nchunks; ++c) {
+    const int v = col[(size_t)c * E];
+    col[(size_t)c * E] = run;
+    run += v;
+  }
+  chunk_tot[e] = run;
+}
+
+// Scatter pass of the multi-block grouping.  Block c reads its bases (routes
+// of each expert in blocks before c) and the totals from the scan pass, scans
+// the totals into the expert offsets, and places its routes at offset + base +
+// rank: the stable order by (expert, token).  Block 0 also writes the offsets
+// and the M-tile tables.
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(
     const DevHandle* __restrict__ table, WaveMap wmap, Hotness hotness, const int32_t* __restrict__ ids, int T, int k, int E,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ chunk_counts, int nchunks,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
-    TileEntry* __restrict__ tiles13, int32_t* __restrict__ ntiles13, int bm13,
-    TileEntry* __restrict__ tiles2, int32_t* __restrict__ ntiles2) {
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ chunk_tot, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
+    int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
+    int32_t* __restrict__ ntiles2) {
   __shared__ int base[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int scan[16];
@@ -499,14 +531,8 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   if (c == 0) src = tile_source(table, wmap, E);   // block 0 writes the tile tables
   int total = 0;
   if (tid < E) {
-    int b = 0, tot = 0;
-    for (int i = 0; i < nchunks; ++i) {
-      const int v = chunk_counts[(size_t)i * E + tid];
-      b += i < c ? v : 0;
-      tot += v;
-    }
-    base[tid] = b;
-    total = tot;
+    base[tid] = chunk_base[(size_t)c * E + tid];
+    total = chunk_tot[tid];
   }
   int all = 0;
   const int excl = block_exclusive_scan(total, scan, all);
@@ -591,7 +617,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
                           int E, int32_t* offsets, int32_t* sorted, int32_t* pos,
                           TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
                           int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,
-                          hipStream_t s) {
+                          int32_t* chunk_tot, hipStream_t s) {
   if (bm13 != bm2) return hipErrorInvalidValue;   // the two GEMMs share one M-tiling
   if (T > kPermSmallT) {
     const int nchunks = (T + kPermChunk - 1) / kPermChunk;
@@ -599,20 +625,21 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
                        chunk_counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(permute_scan_kernel, dim3((E + 255) / 256), dim3(256), 0, s, chunk_counts,
+                       chunk_tot, nchunks, E);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(1024), 0, s, table, wave, hotness, ids, T, k, E,
-                       rank, chunk_counts, nchunks, offsets, sorted, pos, tiles13, ntiles13, bm13,
+                       rank, chunk_counts, chunk_tot, offsets, sorted, pos, tiles13, ntiles13, bm13,
                        tiles2, ntiles2);
     return hipGetLastError();
   }
   const size_t lds = sizeof(int) * (17 * (size_t)E + 1025 + kMaxTileRows);
-  static bool attr_set = false;   // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB)
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(permute_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(sizeof(int) * (17 * kMaxExperts + 1025 + kMaxTileRows)));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB)
+  static DeviceOnce lds_opt_in;
+  const hipError_t ea = ensure_dynamic_lds(lds_opt_in, reinterpret_cast<const void*>(permute_kernel),
+                                           (int)(sizeof(int) * (17 * kMaxExperts + 1025 + kMaxTileRows)));
+  if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, wave, hotness, ids, T, k, E, offsets, sorted,
                      pos, tiles13, ntiles13, bm13, tiles2, ntiles2);
   return hipGetLastError();

@@ -35,6 +35,20 @@ def bf16_dev_to_np(t) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def tile_boundary_tokens(routing, n_experts: int, tile_rows: int) -> np.ndarray:
+    """Tokens owning the first and the last row of every M-tile of the grouped
+    GEMMs: each expert's routes, in the oracle's grouped order, cut into tiles
+    of tile_rows (the library's M-tiling, reported by moe_layer_plan).  Every
+    (M-tile, column block) of both GEMMs then writes into a compared row."""
+    off, srt = routing["offsets"], routing["sorted_routes"]
+    k = routing["ids"].shape[1]
+    pos = []
+    for e in range(n_experts):
+        for a in range(int(off[e]), int(off[e + 1]), tile_rows):
+            pos += [a, min(a + tile_rows, int(off[e + 1])) - 1]
+    return np.unique(srt[np.asarray(pos, dtype=np.int64)] // k)
+
+
 def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
     rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
     return float(np.max(np.abs(y.astype(np.float64) - ref))) / rms

@@ -1,10 +1,20 @@
 """GPU MoE layer forward vs the oracle.
 
-Gate (all configs): max |y_f32 - y_oracle| <= 1e-2 * RMS(y_oracle); the bf16
+Gate (all configs): max |y_f32 - y_oracle| <= tol * RMS(y_oracle); the bf16
 output is bytewise the nearest-even rounding of the f32 output; two runs are
-bytewise identical.  Small configs compare every output; the two largest
-compare sampled tokens at their full size in the launch configuration the
-benchmark times.
+bytewise identical.  The tolerance depends on the grouped-GEMM path the
+library takes for the call (moe_layer_plan):
+  * few routes per expert (path 1): exact integer weight operands and fp32
+    sums, so the result differs from the oracle only by summation order and by
+    the bf16 rounding of an activation that lands on the other side of a
+    rounding boundary (one bf16 ulp, 2^-8 relative, on a few activations):
+    2.5e-3;
+  * many routes per expert (path 2): the dequantized weight is rounded once to
+    fp16 (2^-11 relative per weight), within the 1e-2 layer gate.
+Small configs compare every output; the largest compare every token that owns
+the first or the last row of an M-tile (so every M-tile and column block of
+both GEMMs is checked), at full size, in the launch configuration the
+benchmark times.  The log names each case's path and its error.
 """
 
 import dataclasses
@@ -14,19 +24,23 @@ import pytest
 
 import inputs
 import oracle
-from tests._harness import Setup, bf16_dev_to_np, log, rel_err, to_dev
+from tests._harness import Setup, bf16_dev_to_np, log, rel_err, tile_boundary_tokens, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-2
+TOL = {1: 2.5e-3, 2: 1e-2}   # by moe_layer_plan path
 
 
 def _run(st: Setup, layer=None, subset=None, keep=True, runs=2):
+    """subset: None (every token), a list of tokens, or "tiles" (the tokens
+    owning the first and the last row of every M-tile)."""
     import torch
     if layer is None:
         layer = st.gpu_layer()
     x, wr, b = st.dev_inputs()
-    log(f"forward cfg{st.cfg.cid} T={st.T} tiers={np.bincount(st.tiers, minlength=3).tolist()}")
+    path, bm = layer.plan(st.T)
+    log(f"forward cfg{st.cfg.cid} T={st.T} tiers={np.bincount(st.tiers, minlength=3).tolist()} "
+        f"path={path} tile_rows={bm}")
     y32 = layer.forward(x, wr, b, out_dtype=torch.float32)
     y16 = layer.forward(x, wr, b, out_dtype=torch.bfloat16)
     y32b = layer.forward(x, wr, b, out_dtype=torch.float32) if runs > 1 else y32
@@ -36,12 +50,18 @@ def _run(st: Setup, layer=None, subset=None, keep=True, runs=2):
     assert np.array_equal(y32n.view(np.uint32), y32bn.view(np.uint32)), "not deterministic"
     assert np.array_equal(y16n, oracle.f32_to_bf16_rne(y32n)), "bf16 output != RNE(f32 output)"
     ol = st.oracle_layer()
-    y_ref, _ = ol.forward(st.x, st.wr, st.bias, token_subset=subset, keep=keep)
+    r = oracle.route(st.x, st.wr, st.bias, st.k)
+    if isinstance(subset, str):
+        subset = tile_boundary_tokens(r, st.E, bm)
+        log(f"  comparing {len(subset)} tokens: the first and last row of every M-tile")
+    get = ol.expert if keep else ol._build
+    y_ref = oracle.layer_forward(st.x, r, get, subset)
     got = y32n if subset is None else y32n[subset]
     err = rel_err(got, y_ref)
     got16 = oracle.bf16_bits_to_f32(y16n if subset is None else y16n[subset])
-    log(f"  max|err|/rms f32 = {err:.3e}   bf16 output = {rel_err(got16, y_ref):.3e}")
-    assert err <= TOL
+    log(f"  path {path}: max|err|/rms f32 = {err:.3e} (tol {TOL[path]:.1e})   "
+        f"bf16 output = {rel_err(got16, y_ref):.3e}")
+    assert err <= TOL[path]
     return layer, y32n
 
 
@@ -71,24 +91,22 @@ def test_layer_qwen80b_sweep_full(T):
     _run(Setup(4, T=T), keep=False)
 
 
-def test_layer_qwen80b_1024_sampled():
+def test_layer_qwen80b_1024_full():
     """512 experts at 20 rows per expert on average: the decode kernels with
-    16-row tiles, experts spanning up to four tiles."""
-    st = Setup(4, T=1024)
-    sub = [0, 1, 511, 512, 1000, 1023]
-    _run(st, subset=sub, keep=False)
+    32-row tiles, experts spanning up to four tiles; every output compared."""
+    _run(Setup(4, T=1024), keep=False)
 
 
-def test_layer_qwen80b_4096_sampled():
-    st = Setup(4, T=4096)
-    sub = list(range(0, 4096, 97))[:40] + [4095]
-    _run(st, subset=sub, keep=False)
+def test_layer_qwen80b_4096_tiles():
+    """80 rows per expert: the large-batch kernels with row-aware partial
+    tiles; the first and last row of every M-tile compared."""
+    _run(Setup(4, T=4096), subset="tiles", keep=False)
 
 
-def test_layer_mixtral_prefill_sampled():
-    st = Setup(5)
-    sub = [0, 1, 2, 1000, 2047, 2048, 4095, 4096, 6000, 8190, 8191]
-    _run(st, subset=sub, keep=False, runs=2)
+def test_layer_mixtral_prefill_tiles():
+    """8192 tokens on 8 experts: 256-row tiles, the down GEMM's XCD block
+    remap (K = I = 14336); the first and last row of every M-tile compared."""
+    _run(Setup(5), subset="tiles", keep=False, runs=2)
 
 
 @pytest.mark.parametrize("T", [1, 32, 64])
@@ -97,9 +115,7 @@ def test_layer_mixtral_decode_sampled(T):
     K-chunks: four with 8-row tiles at T = 1 (the last one partial),
     fourteen with 16-row tiles at T = 32, twenty-eight with 32-row tiles at
     T = 64."""
-    st = Setup(5, T=T)
-    sub = [0] if T == 1 else [0, T - 1]
-    _run(st, subset=sub, keep=False, runs=2)
+    _run(Setup(5, T=T), subset="tiles", keep=False, runs=2)
 
 
 def test_layer_decode_ragged_k_chunks():
@@ -202,3 +218,39 @@ def test_handle_swap_promotes_expert():
     st2 = Setup(1, tiers=tiers)
     _, y_after = _run(st2, layer=layer, runs=1)
     assert not np.array_equal(y_before, y_after)
+
+
+def test_plan_query():
+    """moe_layer_plan names the path each workload takes: the decode batches
+    stream weights (path 1), the Mixtral prefill runs on the large-batch
+    kernels (path 2) with 256-row tiles."""
+    assert Setup(2).gpu_layer(experts=[0]).plan(32)[0] == 1
+    assert Setup(5, T=1).gpu_layer(experts=[0]).plan(8192) == (2, 256)
+
+
+def test_large_batch_32bit_offset_limit():
+    """A large-batch forward whose SwiGLU activations [T k, I] (16-bit) would
+    reach 4 GiB is refused on the host with MOE_ESHAPE, before the workspace
+    check; one token fewer passes that check and meets the (deliberately
+    small) workspace instead.  Neither call enqueues any work, so the small
+    x and y buffers are never read."""
+    import torch
+    import mixed_precision_moe_amd as mm
+    from mixed_precision_moe_amd import _lib
+    st = Setup(1, T=8)
+    layer = st.gpu_layer(experts=[0])
+    x, wr, b = st.dev_inputs()
+    T = (1 << 32) // (2 * st.k * st.I)          # T k I 2 bytes = 4 GiB
+    assert layer.plan(T)[0] == 2 and layer.plan(T - 1)[0] == 2
+    y = torch.empty((8, st.H), dtype=torch.float32, device=x.device)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=x.device)
+    lib = _lib.load()
+    s = torch.cuda.current_stream().cuda_stream
+
+    def call(n):
+        return lib.moe_layer_forward(layer._h, x.data_ptr(), wr.data_ptr(), None, n, y.data_ptr(),
+                                     mm.api.DTYPE_F32, ws.data_ptr(), ws.numel(), s)
+    assert call(T) == _lib.MOE_ESHAPE
+    assert b"4 GiB" in lib.moe_last_error()
+    assert call(T - 1) == _lib.MOE_ENOSPC
+    torch.cuda.synchronize()

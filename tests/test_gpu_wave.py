@@ -132,3 +132,31 @@ def test_sequential_per_expert_waves_olmoe():
     err = rel_err(y.cpu().numpy(), y_ref)
     log(f"olmoe sequential {len(touched)} waves: vs oracle {err:.2e}, vs fused {gap:.2e}")
     assert err <= TOL and gap <= 1e-5
+
+
+def test_wave_routing_survives_other_calls_between_waves():
+    """A forward() and a route() of other tokens (same T) between a layer
+    call's waves do not disturb the routing its accumulating waves reuse, and
+    an accumulating wave with no first wave before it is refused."""
+    import torch
+    st = Setup(2, T=32)
+    layer = st.gpu_layer()
+    x, wr, b = st.dev_inputs()
+    x_other = to_dev(np.ascontiguousarray(st.x[::-1]))
+    layer.set_slots(0, layer.handles)
+    half = st.E // 2
+    y = torch.zeros((st.T, st.H), dtype=torch.float32, device=x.device)
+    layer.set_slot_map([e if e < half else -1 for e in range(st.E)])
+    layer.forward_wave(x, wr, b, y=y)
+    layer.forward(x_other, wr, b, out_dtype=torch.float32)
+    layer.route(x_other, wr, b)
+    layer.set_slot_map([e if e >= half else -1 for e in range(st.E)])
+    layer.forward_wave(x, wr, b, y=y, accumulate=True)
+    torch.cuda.synchronize()
+    y_ref, _ = st.oracle_layer().forward(st.x, st.wr, st.bias)
+    err = rel_err(y.cpu().numpy(), y_ref)
+    log(f"two waves around other calls: max|err|/rms = {err:.3e}")
+    assert err <= 2.5e-3
+    layer.set_router_mode(0)                     # drops the waves' routing state
+    with pytest.raises(ValueError):
+        layer.forward_wave(x, wr, b, y=y, accumulate=True)
