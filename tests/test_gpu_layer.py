@@ -6,9 +6,13 @@ bytewise identical.  The tolerance depends on the grouped-GEMM path the
 library takes for the call (moe_layer_plan):
   * few routes per expert (path 1): exact integer weight operands and fp32
     sums, so the result differs from the oracle only by summation order and by
-    the bf16 rounding of an activation that lands on the other side of a
-    rounding boundary (one bf16 ulp, 2^-8 relative, on a few activations):
-    2.5e-3;
+    the bf16 rounding of an activation whose fp32 value (a few fp32 ulps from
+    the oracle's) lands on the other side of a rounding boundary: one bf16 ulp
+    (at most 2^-7 relative) on a few activations.  One such step of the
+    largest activation, through a routing weight and a down-projection weight,
+    moves an output by about 3e-3 of its RMS at the Qwen3-80B shape (I = 512,
+    k = 10, the smallest output RMS per activation); measured up to 2.7e-3
+    there, 2.0e-3 or less elsewhere.  Gate: 4e-3;
   * many routes per expert (path 2): the dequantized weight is rounded once to
     fp16 (2^-11 relative per weight), within the 1e-2 layer gate.
 Small configs compare every output; the largest compare every token that owns
@@ -28,7 +32,7 @@ from tests._harness import Setup, bf16_dev_to_np, log, rel_err, tile_boundary_to
 
 pytestmark = pytest.mark.gpu
 
-TOL = {1: 2.5e-3, 2: 1e-2}   # by moe_layer_plan path
+TOL = {1: 4e-3, 2: 1e-2}   # by moe_layer_plan path
 
 
 def _run(st: Setup, layer=None, subset=None, keep=True, runs=2):
