@@ -296,6 +296,24 @@ int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
                       const float* bias, int32_t T, void* y, int y_dtype, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of moe_layer_forward, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, arguments and results
+ * as moe_layer_forward (bit for bit), but the workspace is a scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on,
+ * from the first call there until the process ends; the call itself allocates
+ * nothing and frees nothing.
+ *   MOE_ENOSPC when moe_workspace_size(layer, T) exceeds the scratch (e.g.
+ *   above about 800 tokens of a Qwen3-30B-A3B-shaped layer); nothing is
+ *   enqueued then.
+ * Every call on one GPU uses that GPU's one scratch array: calls that may
+ * overlap on one GPU (other streams, other threads, other layers) race and
+ * must be ordered by the caller, e.g. on a single stream.  The scratch keeps
+ * the last call's contents; no call relies on them. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
+                              const float* bias, int32_t T, void* y, int y_dtype, void* stream);
+
 /* One wave: as moe_layer_forward, with the router and top-k over all experts
  * unchanged (weights not renormalized within a wave), but only the experts the
  * current slot map sends to a slot contribute, each computed from its slot's

@@ -19,6 +19,7 @@ TIER_BF16, TIER_INT8, TIER_INT4 = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_GATE_UP = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 PATH_DECODE, PATH_LARGE_BATCH = 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 ROUTER_AUTO, ROUTER_CANONICAL, ROUTER_MFMA = 0, 1, 2
 
 # every symbol include/moe.h declares
@@ -28,7 +29,7 @@ EXPORTS = (
     "moe_layer_set_hotness", "moe_plan_tiers", "moe_layer_destroy", "moe_workspace_size",
     "moe_route", "moe_layer_forward", "moe_layer_forward_wave", "moe_layer_set_stage_events",
     "moe_layer_set_router_mode", "moe_strerror", "moe_last_error", "moe_abi_version",
-    "moe_unpack_codes", "moe_layer_plan",
+    "moe_unpack_codes", "moe_layer_plan", "moe_layer_forward_noalloc",
 )
 
 
@@ -87,6 +88,7 @@ def load() -> ctypes.CDLL:
         "moe_abi_version": (ctypes.c_int, []),
         "moe_unpack_codes": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, vp, sz, i64, i64, vp, vp]),
         "moe_layer_plan": (ctypes.c_int, [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "moe_layer_forward_noalloc": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

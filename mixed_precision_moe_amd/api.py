@@ -211,6 +211,21 @@ class Layer:
                                           _stream(stream)), "moe_layer_forward")
         return y
 
+    def forward_noalloc(self, x: torch.Tensor, wr: torch.Tensor, y: torch.Tensor,
+                        bias: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """moe_layer_forward_noalloc: the same forward with the library's fixed
+        per-device scratch as workspace; y must be given (nothing is allocated)."""
+        _require_cuda(x, "x", _BF16)
+        _require_cuda(wr, "wr", _BF16)
+        _require_cuda(y, "y", (torch.float32, torch.bfloat16))
+        if bias is not None:
+            _require_cuda(bias, "bias", (torch.float32,))
+        check(self._lib.moe_layer_forward_noalloc(self._h, x.data_ptr(), wr.data_ptr(), _ptr(bias),
+                                                  x.shape[0], y.data_ptr(),
+                                                  DTYPE_F32 if y.dtype == torch.float32 else DTYPE_BF16,
+                                                  _stream(stream)), "moe_layer_forward_noalloc")
+        return y
+
     def bind_forward(self, x: torch.Tensor, wr: torch.Tensor, bias: Optional[torch.Tensor],
                      y: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None):
         """A zero-argument callable that enqueues one forward with these fixed

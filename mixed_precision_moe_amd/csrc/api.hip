@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "device_util.h"
@@ -665,3 +666,70 @@ int moe_layer_forward_wave(moe_layer_t layer, const uint16_t* x, const uint16_t*
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  Its workspace is `scratch`, a file-scope device
+// array (one per GPU, held by the loaded library until the process ends).  In
+// host code the array's name only stands in for it; its device address on
+// each GPU comes from hipGetSymbolAddress, asked once per device with that
+// device current, and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (set up on its first use
+// there).
+int scratch_address(void** out) {
+  int dev = -1;
+  int rc = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(MOE_EINVAL, "device %d: the allocation-free forward serves devices 0..%d", dev,
+                     kMaxDevices - 1);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+      if (rc) return rc;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_layer_forward_noalloc(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
+                                         const float* bias, int32_t T, void* y, int y_dtype,
+                                         void* stream) {
+  g_err[0] = 0;
+  const Layer* L = reinterpret_cast<const Layer*>(layer);
+  if (!L) return set_error(MOE_EINVAL, "null layer");
+  if (T < 0 || T > (1 << 24)) return set_error(MOE_ESHAPE, "bad token count %d", T);
+  const size_t need = moe_workspace_size(layer, T);
+  if (need > kScratchBytes)
+    return set_error(MOE_ENOSPC,
+                     "%d tokens need %zu bytes of workspace; the allocation-free forward has a "
+                     "fixed scratch of %zu bytes per device (use moe_layer_forward with a "
+                     "workspace, or fewer tokens per call)",
+                     T, need, kScratchBytes);
+  if (T == 0)
+    return forward_impl(L, WaveMap{nullptr, nullptr}, false, x, wr, bias, T, y, y_dtype, nullptr, 0,
+                        stream);
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  // every workspace region a forward reads is written earlier in the same
+  // forward, so nothing needs clearing between calls
+  return forward_impl(L, WaveMap{nullptr, nullptr}, false, x, wr, bias, T, y, y_dtype, ws,
+                      kScratchBytes, stream);
+}
