@@ -274,6 +274,10 @@ def main():
     ap.add_argument("--no-dense-reference", action="store_true",
                     help="skip timing the vendor dense GEMM of the same total shape beside an "
                          "MFMA-bound gate/up kernel")
+    ap.add_argument("--prefill-config", type=int, default=5,
+                    help="also measure this config at its default token count as the large-batch "
+                         "record ('prefill' in the JSON); 0 to skip")
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run plain device copies of this many MiB (for scaling HBM "
                          "counters) and exit")
@@ -308,6 +312,53 @@ def main():
         return
     cfg = inputs.get_config(args.config)
     T = cfg.default_tokens if args.tokens is None else args.tokens
+    m = measure(cfg, T, args.steps, args.warmup, args, dev)
+    out = {
+        "metric": METRIC,
+        "value": m["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": m["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": m["config"],
+        "roofline": m["roofline"],
+    }
+    if args.compare_sequential:
+        out["comparison"] = compare_sequential(m["layers"][0], m["x"], m["wr"], m["bias"], m["ids"], T,
+                                               cfg.hidden, dev, m["fwd"][0],
+                                               max(5, min(args.steps, 50)))
+    for L in m["layers"]:
+        L.close()
+    if args.prefill_config and args.prefill_config != args.config:
+        # the large-batch record: the Mixtral-shaped 8192-token prefill, where
+        # the gate/up kernel is MFMA-bound; timed the same way, fewer steps
+        pcfg = inputs.get_config(args.prefill_config)
+        pm = measure(pcfg, pcfg.default_tokens, max(4, min(args.steps, args.prefill_steps)),
+                     min(args.warmup, 3), args, dev)
+        for L in pm["layers"]:
+            L.close()
+        out["prefill"] = {"value": pm["value"], "unit": "tokens/s", "ms_per_step": pm["ms_per_step"],
+                          "steps": pm["steps"], "config": pm["config"], "roofline": pm["roofline"]}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, m["tiers"], m["x_np"], m["wr_np"], m["bias_np"])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def measure(cfg, T, steps, warmup, args, dev):
+    """Time whole-layer forwards of one workload: a host-launched region with
+    per-stage events (and the gate/up kernel's own start and end), then a HIP
+    graph of R forwards (one per weight copy) replayed back to back, from which
+    the throughput is taken."""
+    import torch
     tiers = inputs.gen_tiers(cfg)
     x_np, wr_np, bias_np = inputs.gen_tokens(cfg, T), inputs.gen_router(cfg), inputs.gen_bias(cfg)
     total_w = sum(packed_bytes(int(tiers[e]), 2 * cfg.inter, cfg.hidden) +
@@ -326,17 +377,19 @@ def main():
     ws = torch.empty(layers[0].workspace_size(T), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     fwd = [L.bind_forward(x, wr, bias, y, workspace=ws, stream=stream) for L in layers]
+    path, tile_rows = layers[0].plan(T)
 
     # routing (for the algorithmic byte/flop counts): outside the timed region
     route = layers[0].route(x, wr, bias)
     ids = route["ids"].cpu().numpy()
+    del route
     alg = algorithmic(cfg, tiers, ids, T)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         fwd[i % R]()
     torch.cuda.synchronize()
 
-    K = args.steps
+    K = steps
     # Timed region 1: one host launch per forward, HIP events recorded on the
     # forward's stream around every stage (the per-kernel durations).
     # events 0..6: stage boundaries; 7, 8: the gate/up GEMM kernel's own start
@@ -376,10 +429,12 @@ def main():
         end.record(stream)
         torch.cuda.synchronize()
         total_ms, launch = start.elapsed_time(end), f"HIP graph of {R} forwards, replayed"
+        del graph
     stage_avg_us = (stage_ms.mean(axis=0) * 1000).round(2)
     ms_per_step = total_ms / K
     value = T * K / (total_ms / 1000.0)
-    log(f"[bench] gate/up GEMM kernel (own timestamps): {g13_kernel_us:.2f} us")
+    log(f"[bench] {ms_per_step * 1000:.2f} us per layer; gate/up GEMM kernel (own timestamps): "
+        f"{g13_kernel_us:.2f} us")
     log("[bench] stage averages (us): " +
         ", ".join(f"{n}={v}" for n, v in zip(STAGES, stage_avg_us)))
 
@@ -410,41 +465,23 @@ def main():
 
     layer_roof_s = max(alg["bytes_layer"] / (HBM_PEAK_GBS * 1e9),
                        alg["flops_layer"] / (BF16_PEAK_TFLOPS * 1e12))
-    out = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": cfg.describe(T),
-            "tokens": T, "hidden": cfg.hidden, "experts": cfg.n_experts, "top_k": cfg.top_k,
-            "inter": cfg.inter, "touched_experts": alg["touched"],
-            "weight_copies_rotated": R, "output": args.out_dtype,
-            "launch": launch, "ms_per_step_host_launch": round(eager_ms / args.steps, 4),
-            "layer_roofline_frac": round(layer_roof_s / (ms_per_step / 1000.0), 4),
-            "stage_avg_us": dict(zip(STAGES, [float(v) for v in stage_avg_us])),
-        },
-        "roofline": roof,
+    config = {
+        "workload": cfg.describe(T),
+        "tokens": T, "hidden": cfg.hidden, "experts": cfg.n_experts, "top_k": cfg.top_k,
+        "inter": cfg.inter, "touched_experts": alg["touched"],
+        "gemm_path": {1: "few routes per expert (weight streaming)",
+                      2: "many routes per expert (fp16 MFMA)"}.get(path, str(path)),
+        "tile_rows": tile_rows,
+        "weight_copies_rotated": R, "output": args.out_dtype,
+        "launch": launch, "ms_per_step_host_launch": round(eager_ms / steps, 4),
+        "layer_roofline_frac": round(layer_roof_s / (ms_per_step / 1000.0), 4),
+        "layer_bound": "mfma" if alg["flops_layer"] / (BF16_PEAK_TFLOPS * 1e12) >
+                       alg["bytes_layer"] / (HBM_PEAK_GBS * 1e9) else "hbm",
+        "stage_avg_us": dict(zip(STAGES, [float(v) for v in stage_avg_us])),
     }
-    if args.compare_sequential:
-        out["comparison"] = compare_sequential(layers[0], x, wr, bias, ids, T, cfg.hidden, dev,
-                                               fwd[0], max(5, min(args.steps, 50)))
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, tiers, x_np, wr_np, bias_np)
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
-    for L in layers:
-        L.close()
+    return dict(value=round(value, 1), steps=K, ms_per_step=round(ms_per_step, 5), config=config,
+                roofline=roof, layers=layers, fwd=fwd, x=x, wr=wr, bias=bias, ids=ids, tiers=tiers,
+                x_np=x_np, wr_np=wr_np, bias_np=bias_np)
 
 
 if __name__ == "__main__":
