@@ -44,15 +44,23 @@ typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v4u32 lds_u4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) float lds_f32;
 typedef short f16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
 
 constexpr int PBM = 256, PBN = 256, PBK = 64;
 constexpr int kPrefillThreads = 512;
 constexpr int kFragBytes = 1024;                         // one 16 x 32 fp16 operand
 constexpr int kPanelBytes = 2 * (PBM / 16) * kFragBytes; // A or B of one chunk: 32 fragments
+// LDS activation buffers of the int4 path: the chunk being read and the one
+// in flight.  Three (a DMA two chunks ahead) measured slower on every large-
+// batch workload: the workgroup fence of __syncthreads() waits for every LDS
+// DMA in flight, and a bare s_barrier with explicit waits cost more than the
+// deeper prefetch saved.
+constexpr int kAStages = 2;
 // 2 buffers x (activations + staged weights) = 128 KB; the int4 path uses the
 // activation half only
 constexpr size_t kPrefillLds = (size_t)2 * 2 * kPanelBytes;
+static_assert(kAStages * kPanelBytes <= (int)kPrefillLds, "int4 activation buffers fit the block's LDS");
 
 struct PrefillArgs {
   const TileEntry* tiles;
@@ -73,13 +81,20 @@ struct PrefillArgs {
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
-// fp16 magic: 0x6400 | u is the fp16 value 1024 + u for u < 1024.
-__device__ __forceinline__ void dequant_int4_word(uint32_t w, half2_t s2, uint32_t out[4]) {
-  const uint32_t mask = 0x000f000fu, magic = 0x64006400u;
+// fp16 magic: 0x6400 | u is the fp16 value 1024 + u for u < 1024.  The mask
+// and magic come from fp16_int4_consts() (an SGPR and a VGPR the compiler
+// cannot see through), so each element pair is one v_and_or_b32 (after a
+// shift for pairs 1..3) instead of an and and an or with literals.
+__device__ __forceinline__ Int4Consts fp16_int4_consts() {
+  return Int4Consts{opaque_sgpr(0x000f000fu), opaque_vgpr(0x64006400u)};
+}
+
+__device__ __forceinline__ void dequant_int4_word(uint32_t w, half2_t s2, uint32_t out[4],
+                                                  Int4Consts c) {
   const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t t = ((w >> (4 * j)) & mask) | magic;     // elements 2j, 2j+1
+    const uint32_t t = ((w >> (4 * j)) & c.mask) | c.magic;  // elements 2j, 2j+1
     const half2_t q = as_h2(t) + bias;                       // exact: q in [-8, 7]
     out[j] = as_u32(q * s2);                                 // fp16(q * s)
   }
@@ -161,10 +176,11 @@ __device__ __forceinline__ void store_b_chunk(const BStage<TIER>& raw, float row
   if constexpr (TIER == MOE_TIER_INT4) {
     const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)raw.scale);
     const half2_t s2 = {sh, sh};
+    const Int4Consts k4 = fp16_int4_consts();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint32_t o[4];
-      dequant_int4_word(raw.w[c], s2, o);
+      dequant_int4_word(raw.w[c], s2, o, k4);
       put(c, o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (TIER == MOE_TIER_INT8) {
@@ -206,15 +222,15 @@ __device__ __forceinline__ f16x8_t pack_f16x8(uint32_t x0, uint32_t x1, uint32_t
 }
 
 // Dequantize the chunk's int4 codes into the B operands of both k-steps.
-__device__ __forceinline__ void dequant_b(const BDirect& raw, f16x8_t (&fb)[2][4]) {
+__device__ __forceinline__ void dequant_b(const BDirect& raw, f16x8_t (&fb)[2][4], Int4Consts k4) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const _Float16 sh = (_Float16)half_of(raw.scale, j);
     const half2_t s2 = {sh, sh};
     uint32_t o[4];
-    dequant_int4_word(raw.w[j].x, s2, o);
+    dequant_int4_word(raw.w[j].x, s2, o, k4);
     fb[0][j] = pack_f16x8(o[0], o[1], o[2], o[3]);
-    dequant_int4_word(raw.w[j].y, s2, o);
+    dequant_int4_word(raw.w[j].y, s2, o, k4);
     fb[1][j] = pack_f16x8(o[0], o[1], o[2], o[3]);
   }
 }
@@ -236,17 +252,28 @@ struct RowWork {
   __device__ bool any(int wm) const { return 128 * wm < rows; }
 };
 
+// Tiles of at most 128 rows (KSPLIT): the two wave rows split K instead of M.
+// Wave (h, wn) takes the 64-wide chunks 2j + h of K for all of the tile's rows,
+// so every wave of the block loads weights and runs MFMAs and the block needs
+// half the K steps; a step's LDS buffer holds chunk 2j in 16-row blocks 0..7
+// and chunk 2j + 1 in blocks 8..15.  The two halves' sums meet in LDS after the
+// loop (even chunks + odd chunks, a fixed order).
+constexpr int kSplitKMaxRows = 128;
+
 // int4 tier: weights straight from memory into MFMA operands.
-template <bool GATE_UP, bool FULL>
+template <bool GATE_UP, bool FULL, bool KSPLIT>
 __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, const uint8_t* blob,
                                                         const int (&arow)[4], int n_block,
                                                         lds_u8* lds, f32x4_t (&acc)[8][4],
                                                         RowWork rw) {
+  static_assert(!(FULL && KSPLIT), "split K serves partial tiles");
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const bool wave_b = FULL || rw.any(wm);               // this wave needs weights
+  const int rm = KSPLIT ? 0 : wm;                       // the wave's row half of the tile
+  const bool wave_b = FULL || rw.any(rm);               // this wave needs weights
   const int K = a.K, G = K / kGroup, KC = K / PBK;
-  constexpr int kWaitVmcntB = wait_vmcnt(5);            // one chunk's weight loads per lane
+  // steps of the loop: one chunk per wave each (KSPLIT: two chunks per block)
+  const int NJ = KSPLIT ? KC / 2 : KC;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<MOE_TIER_INT4>(a.N, K));
   const int quad = n_block / 64 + wn;                   // this wave's quad (wave-uniform)
   constexpr int kBlk = PTier<MOE_TIER_INT4>::kBlock;
@@ -254,12 +281,14 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   // chunk values (128 B) with the 8-value slice kb in 16-byte slot kb ^ (rr/2).
   // Staging role: wave w fills tile rows 32w .. 32w+31 with 4 DMAs; lane l of
   // DMA i loads tile row 32w + 8i + l/8 into slot l%8.
+  // KSPLIT: waves 4..7 stage the odd chunk of each step, 128 bytes further on
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a.a16, a.a16_bytes);
   uint32_t avoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = 8 * (i & 1) + (lane >> 3);              // row within the 16-row block
-    avoff[i] = (uint32_t)arow[i] * K * 2u + 16u * ((lane & 7) ^ (rr >> 1));
+    avoff[i] = (uint32_t)arow[i] * K * 2u + 16u * ((lane & 7) ^ (rr >> 1)) +
+               (KSPLIT ? 2u * PBK * (uint32_t)wm : 0u);
   }
   // operand read offsets within a 16-row block, k-steps 0 and 1
   uint32_t aread[2];
@@ -269,6 +298,9 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
     aread[ks] = 128u * rr + 16u * (kb ^ (rr >> 1));
   }
   auto As = [&](int buf) { return lds + buf * kPanelBytes; };
+  const Int4Consts k4 = fp16_int4_consts();
+  // K chunk of this wave in loop step j
+  auto chunk_of = [&](int j) { return KSPLIT ? 2 * j + wm : j; };
 
   // weights of chunk c travel in register slot c % 2, two chunks ahead
   BDirect braw0, braw1;
@@ -279,13 +311,14 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
     for (int j = 0; j < 4; ++j) raw.w[j] = buffer_load8(rsrc, 16 * lane + 1024 * j, block + 8 * (kc & 1));
     raw.scale = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
   };
-  auto dma_a = [&](int kc, int buf) {
-    if (!FULL && !rw.dma(wave)) return;
+  // activations of step j (KSPLIT: chunks 2j and 2j + 1)
+  auto dma_a = [&](int j, int buf) {
+    if (!FULL && !rw.dma(KSPLIT ? (wave & 3) : wave)) return;
     lds_u8* dst = As(buf) + 4 * wave * 1024;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
-                                               2u * PBK * kc, 0, 0);
+                                               2u * PBK * (KSPLIT ? 2 * j : j), 0, 0);
   };
 
   f16x8_t fa[2][8], fb[2][4];
@@ -293,7 +326,7 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
     const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      if (FULL || rw.blk(wm, 4 * h)) {
+      if (FULL || rw.blk(rm, 4 * h)) {
 #pragma unroll
         for (int i = 4 * h; i < 4 * h + 4; ++i)
           fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
@@ -302,7 +335,7 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   auto mfma_block = [&](int ks) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      if (FULL || rw.blk(wm, 4 * h)) {
+      if (FULL || rw.blk(rm, 4 * h)) {
 #pragma unroll
         for (int i = 4 * h; i < 4 * h + 4; ++i)
 #pragma unroll
@@ -310,33 +343,68 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
       }
   };
 
-  // One chunk: its successor's activations stream into the other buffer by
-  // DMA; this chunk's weights (loaded two chunks ago) are dequantized into
-  // MFMA operands and their register slot refilled with the weights two
-  // chunks ahead.  Prefetch indices are clamped at the end of K (a repeated
-  // load of the last chunk, never used), so the body has no branches and the
-  // compiler's load waits stay exact.  KC is even (K is a multiple of 128):
-  // unrolled by two, each register slot keeps its role.
-  auto step = [&](int kc, BDirect& raw) {
-    const int buf = kc & 1;
-    dma_a(min(kc + 1, KC - 1), buf ^ 1);
-    if (wave_b) dequant_b(raw, fb);
-    load_b(min(kc + 2, KC - 1), raw);
+  // One step: the activations kAStages - 1 steps ahead stream into a free
+  // LDS buffer by DMA; this chunk's weights (loaded two chunks ago) are
+  // dequantized into MFMA operands and their register slot refilled with the
+  // weights two chunks ahead.  Prefetch indices are clamped at the end of K (a
+  // repeated load of the last chunk, never used), so the body has no branches
+  // and the compiler's load waits stay exact.  KC is even (K is a multiple of
+  // 128): unrolled by two, each register slot keeps its role.  Before the
+  // chunk's barrier each wave waits for its DMA of the next chunk; what it
+  // issued after that DMA (weights, later DMAs) may stay in flight: 5 loads per
+  // chunk of weights, 4 per chunk of activations.
+  constexpr int kAhead = kAStages - 1;
+  constexpr int kWaitNext = wait_vmcnt(5 + (kAhead - 1) * 9);
+  auto step = [&](int j, BDirect& raw) {
+    const int buf = j % kAStages;
+    dma_a(min(j + kAhead, NJ - 1), (j + kAhead) % kAStages);
+    if (wave_b) dequant_b(raw, fb, k4);
+    load_b(chunk_of(min(j + 2, NJ - 1)), raw);
     read_frags(buf, 0);
     read_frags(buf, 1);
     mfma_block(0);
     mfma_block(1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcntB);   // the successor's DMA is done; the weights ahead may fly
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
     __syncthreads();
   };
-  load_b(0, braw0);
-  load_b(1, braw1);
-  dma_a(0, 0);
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  load_b(chunk_of(0), braw0);
+  load_b(chunk_of(min(1, NJ - 1)), braw1);
+#pragma unroll
+  for (int c = 0; c < kAhead; ++c) dma_a(min(c, NJ - 1), c);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt((kAhead - 1) * 4));   // step 0 is in LDS
   __syncthreads();
-  for (int kc = 0; kc < KC; kc += 2) {
-    step(kc, braw0);
-    step(kc + 1, braw1);
+  int j = 0;
+  for (; j + 2 <= NJ; j += 2) {
+    step(j, braw0);
+    step(j + 1, braw1);
+  }
+  if (j < NJ) step(j, braw0);   // KSPLIT with K / 128 odd: one step left
+  if constexpr (KSPLIT) {
+    // the odd chunks' sums (wave row 1) join the even chunks' (wave row 0) in
+    // LDS, which the loop's last barrier has freed; only 16-row blocks with a
+    // real row travel
+    lds_f32* red = reinterpret_cast<lds_f32*>(lds) + wn * 8 * 4 * 4 * 64;
+    if (wm == 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (rw.blk(0, i)) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((i * 4 + jj) * 4 + e) * 64 + lane] = acc[i][jj][e];
+        }
+    }
+    __syncthreads();
+    if (wm == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (rw.blk(0, i)) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][jj][e] += red[((i * 4 + jj) * 4 + e) * 64 + lane];
+        }
+    }
   }
 }
 
@@ -499,10 +567,14 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
   const RowWork rw{te.rows};
   const bool full = te.rows >= PBM;          // tile-uniform
   if constexpr (TIER == MOE_TIER_INT4) {
-    if (full)
-      prefill_mainloop_direct<GATE_UP, true>(a, blob, arow, n_block, plds, acc, rw);
-    else
-      prefill_mainloop_direct<GATE_UP, false>(a, blob, arow, n_block, plds, acc, rw);
+    if (full) {
+      prefill_mainloop_direct<GATE_UP, true, false>(a, blob, arow, n_block, plds, acc, rw);
+    } else if (te.rows <= kSplitKMaxRows) {
+      prefill_mainloop_direct<GATE_UP, false, true>(a, blob, arow, n_block, plds, acc, rw);
+      if (wm == 1) return;                   // its sums went to wave row 0
+    } else {
+      prefill_mainloop_direct<GATE_UP, false, false>(a, blob, arow, n_block, plds, acc, rw);
+    }
   } else {
     prefill_mainloop_staged<TIER, GATE_UP, true>(a, blob, arow, n_block, plds, acc, rw);
   }
@@ -570,13 +642,16 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
   const int tid = threadIdx.x;
   const int n_block = nb * PBN;
 
-  // activation rows this thread's lane loads: row 32 wave + 8 i + lane / 8;
-  // rows past the tile's count read the tile's last row (their results are
-  // never stored)
+  // activation rows this thread's lane loads: row 32 wave + 8 i + lane / 8
+  // (int4 tiles of at most 128 rows, whose wave rows split K: row
+  // 32 (wave % 4) + 8 i + lane / 8); rows past the tile's count read the
+  // tile's last row (their results are never stored)
+  const bool ksplit = te.tier == MOE_TIER_INT4 && te.rows <= kSplitKMaxRows;   // tile-uniform
+  const int wrow = ksplit ? (tid >> 6) & 3 : tid >> 6;
   int arow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = min(32 * (tid >> 6) + 8 * j + ((tid & 63) >> 3), te.rows - 1);
+    const int m = min(32 * wrow + 8 * j + ((tid & 63) >> 3), te.rows - 1);
     const int pos = te.row_start + m;
     arow[j] = GATE_UP ? a.sorted[pos] / a.top_k : pos;
   }

@@ -146,9 +146,10 @@ constexpr double kDecodeRowsMaxWide = 40.0;
 __host__ __device__ constexpr int decode_rstride(int rows) { return rows > 16 ? rows : 16; }
 // A columns staged per chunk (multiples of kGroup): 4096 for 8-row tiles;
 // 1024 for 16-row and 512 for 32-row tiles, so that a chunk stays near 33 KB
-// of LDS and four blocks fit a CU
+// of LDS and four blocks fit a CU; 512 for 64-row and 256 for 128-row tiles
+// (about 67 KB: two blocks per CU, as their two waves per SIMD allow)
 __host__ __device__ constexpr int decode_chunk_cap(int rows) {
-  return rows == 8 ? 4096 : rows == 16 ? 1024 : 512;
+  return rows == 8 ? 4096 : rows == 16 ? 1024 : rows == 128 ? 256 : 512;
 }
 __host__ __device__ constexpr int decode_chunk_k(int K, int rows) {
   return K < decode_chunk_cap(rows) ? K : decode_chunk_cap(rows);
@@ -209,11 +210,15 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
 
   // consume(g, d): k-group g (absolute), whose weights are in set d and whose
   // A columns and group sums sit at chunk-relative group g - c0 in LDS
+  // 16-row MFMA blocks holding a real row of the tile (the others are skipped:
+  // their rows are never stored)
+  const int nrb = uniform((rows + 15) >> 4);
   int c0 = 0;
   auto consume = [&](int g, int d) {
     const int gl = g - c0;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {   // 32-row tiles: both MFMA blocks take each weight load
+    for (int rb = 0; rb < RB; ++rb) {   // tiles of 32+ rows: every MFMA block takes each weight load
+      if (RB > 2 && rb >= nrb) break;
       f32x4_t p[NS];
       if constexpr (TIER == MOE_TIER_BF16) {
 #pragma unroll
@@ -382,7 +387,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const int chunk = KSPLIT ? nb : nb * WAVES + wave;   // this wave's group of NS strips
   const int strip0 = chunk * NS;
   uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
-  static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "an M-tile is 8, 16 or 32 rows");
+  static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32 || ROWS == 64 || ROWS == 128,
+                "an M-tile is 8, 16, 32, 64 or 128 rows");
   constexpr int RB = ROWS > 16 ? ROWS / 16 : 1;   // 16-row MFMA blocks per tile
   float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)ROWS * (decode_chunk_k(a.K, ROWS) + 8) * 2);
 
@@ -513,9 +519,16 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
   using R8 = std::integral_constant<int, 8>;
   using R16 = std::integral_constant<int, 16>;
   using R32 = std::integral_constant<int, 32>;
+  using R64 = std::integral_constant<int, 64>;
+  using R128 = std::integral_constant<int, 128>;
   if (rows == 8) return ksplit ? run(std::true_type{}, R8{}) : run(std::false_type{}, R8{});
   if (rows == 16) return ksplit ? run(std::true_type{}, R16{}) : run(std::false_type{}, R16{});
   if (rows == 32) return ksplit ? run(std::true_type{}, R32{}) : run(std::false_type{}, R32{});
+  // tiles of 64 and 128 rows serve forwards with tens of routes per expert:
+  // many tiles, never split K
+  if (ksplit) return hipErrorInvalidValue;
+  if (rows == 64) return run(std::false_type{}, R64{});
+  if (rows == 128) return run(std::false_type{}, R128{});
   return hipErrorInvalidValue;
 }
 
@@ -632,7 +645,8 @@ hipError_t launch_gemm13(const Layer& L, const GemmPlan& gp, int T, const uint16
   a.r2 = r2;
   a.I = L.I;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  return launch_decode<4, true>(a, max_tiles, gp.bm13, decode_split_k(L, T, a.N), s, kt);
+  return launch_decode<4, true>(a, max_tiles, gp.bm13, gp.bm13 < 64 && decode_split_k(L, T, a.N), s,
+                                kt);
 }
 
 hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_t* act,
@@ -651,7 +665,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.topk_w = topk_w;
   a.rows = rows;
   if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
-  const bool ks = decode_split_k(L, T, a.N);
+  const bool ks = gp.bm2 < 64 && decode_split_k(L, T, a.N);
   // Very few column blocks even with split K (a wide-K, narrow-N down GEMM
   // over one or two tiles, e.g. the Mixtral shape at one token): two strips
   // per wave double the blocks.  Mixtral T = 1: 64.9 -> 61.3 us per layer;

@@ -130,6 +130,23 @@ def test_layer_decode_ragged_k_chunks():
     _run(Setup(1, T=16, cfg=c, tiers=np.array([2, 1, 0, 2])), keep=False)
 
 
+@pytest.mark.parametrize("T", [65, 100, 128, 129, 200])
+def test_layer_large_batch_ragged_k(T):
+    """The large-batch kernels on a layer whose K-chunk counts are odd
+    (hidden 4352, inter 4224: 34 and 33 steps of two 64-wide chunks), all
+    routes on experts 0 (int4) and 3 (int8) at T rows each: int4 tiles of at
+    most 128 rows split K between the block's two wave rows (the down GEMM
+    with a last single step), larger ones split rows."""
+    c = dataclasses.replace(inputs.get_config(1), hidden=4352, inter=4224, n_experts=4,
+                            top_k=2, max_tokens=200)
+    b = np.zeros(4, np.float32)
+    b[[0, 3]] = 100.0
+    st = Setup(1, T=T, cfg=c, bias=b, tiers=np.array([2, 0, 2, 1]))
+    layer = st.gpu_layer(experts=[0, 3])
+    assert layer.plan(T)[0] == 2
+    _run(st, layer=layer, keep=False, runs=1)
+
+
 @pytest.mark.parametrize("tier", [0, 1, 2])
 def test_layer_single_tier(tier):
     st = Setup(1, tiers=np.full(8, tier))
