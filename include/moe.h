@@ -199,9 +199,9 @@ int moe_layer_set_slots(moe_layer_t layer, int32_t first, int32_t count,
                         const moe_expert_handle* handles, void* stream);
 int moe_layer_set_slot_map(moe_layer_t layer, const int32_t* expert_to_slot, void* stream);
 
-/* DynaExq (abstract): expert hotness is estimated from router traces over a
- * long horizon; a budget-feasible top-n rule picks the per-layer set kept at
- * high precision; promotions and demotions go through stable handles
+/* DynaExq (abstract): each expert's usage is estimated from the routing over
+ * time; the experts kept at high precision are the most used ones that fit a
+ * memory budget; version changes go through stable handles
  * (moe_layer_set_experts) so every forward runs on fully materialized experts.
  *
  * moe_layer_set_hotness: from the next call on, every moe_layer_forward (and

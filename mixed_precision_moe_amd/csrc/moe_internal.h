@@ -94,7 +94,7 @@ struct Layer {
   DevHandle* slots;      // device [E]
   int32_t* slot_map;     // device [E]
   uint8_t* slot_set;     // host [E]
-  // long-horizon hotness: each forward sets hot[e] = decay * hot[e] + its
+  // usage trace over many calls: each forward sets hot[e] = decay * hot[e] + its
   // routes to e (caller-owned device [E], or null)
   float* hot;
   float hot_decay;

@@ -1,9 +1,10 @@
 """Online precision allocation for one layer ("Dynamic Expert Quantization for
-Scalable Mixture-of-Experts Inference", abstract): expert hotness estimated
-from the router trace over a long horizon, a budget-feasible top-n rule for the
-set kept at high precision, and promotions / demotions applied asynchronously
-through the layer's stable expert handles, so every forward runs on fully
-materialized expert versions.
+Scalable Mixture-of-Experts Inference", abstract).  Each expert's usage is
+counted from the layer's own routing, with an optional decay; the n most used
+experts that fit a memory budget are held at the high precision tier and the
+rest at the low one; version changes are repacked off the forward stream and
+swapped in through the layer's stable expert handles, so a forward never sees
+a half-written expert.
 
 Every step is a library call: the grouping kernel keeps the decayed route
 counts on the device (moe_layer_set_hotness), moe_plan_tiers makes the plan,

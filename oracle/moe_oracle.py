@@ -371,8 +371,8 @@ def wave_forward(x_bf16: np.ndarray, routing: Dict[str, np.ndarray],
 
 
 def plan_tiers(hot, bytes_per_tier, budget_bytes: int, hi_tier: int, lo_tier: int):
-    """[DynaExq] (abstract): a budget-feasible top-n rule selects the experts
-    kept at high precision.  Reading: rank experts by hotness (descending,
+    """[DynaExq] (abstract): the experts kept at high precision are chosen by
+    usage rank within a memory budget.  Reading: rank experts by hotness (descending,
     ties to the lower id); the n hottest take hi_tier, the rest lo_tier, with n
     the largest count whose total bytes fit the budget.  Returns (tiers, n);
     raises ValueError when all experts at lo_tier already exceed it."""

@@ -1,4 +1,5 @@
-"""DynaExq's budget-feasible top-n tier plan (CPU only).
+"""DynaExq's tier plan: the n most used experts that fit a byte budget take the
+high tier (CPU only).
 
 The oracle's rule is pinned by brute force over every subset of a small
 expert set (the chosen set is the largest feasible one made of the hottest

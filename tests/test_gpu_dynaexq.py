@@ -1,6 +1,6 @@
 """DynaExq online loop on the GPU ("Dynamic Expert Quantization for Scalable
-Mixture-of-Experts Inference", abstract): hotness from the router trace,
-budget-feasible top-n plan, asynchronous repack, promotion through the stable
+Mixture-of-Experts Inference", abstract): usage counted from the routing,
+budgeted plan of the most used experts, asynchronous repack, promotion through the stable
 handle table.
 
 * The hotness trace equals the oracle's route counts exactly (plain counts and
