@@ -10,25 +10,31 @@ Shapes follow the layer geometries the MoE pages discuss: a tiny layer, a
 Qwen3-30B-A3B-shaped layer (decode and a skewed mixed-precision batch), a
 Qwen3-80B-shaped layer with many small experts, and a Mixtral-shaped layer
 for prefill.  The mixed-precision hot sets follow the DynaExq idea (Dynamic
-Expert Quantization, abstract): the most popular experts are held at higher
-precision, the rest at an int4 fallback.  Here popularity is the prior the
-workload is built from (the Zipf rank that sets the router bias), so the tier
-table is an input and needs no routing to construct.
+Expert Quantization, abstract): the most used experts are held at higher
+precision, the rest at an int4 fallback.  Usage is the routes counted over
+the workload's full token set; the ranking is a stored table
+(hot_sets.json beside this file, written by tests/golden/make_hot_sets.py),
+so this module itself does no routing.
 """
 
 from __future__ import annotations
 
 import dataclasses
+import functools
+import json
+import os
 from typing import Dict, Optional, Tuple
 
 import numpy as np
+
+HOT_SETS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hot_sets.json")
 
 TIER_BF16 = 0
 TIER_INT8 = 1
 TIER_INT4 = 2
 
 # stream ids inside one config's seed tuple
-_S_TOKENS, _S_ROUTER, _S_BIAS, _S_TIERS, _S_EXPERT = 0, 1, 2, 3, 4
+_S_TOKENS, _S_ROUTER, _S_BIAS, _S_EXPERT = 0, 1, 2, 4
 
 WEIGHT_STD = 0.02
 
@@ -140,19 +146,34 @@ def gen_bias(cfg: LayerConfig) -> Optional[np.ndarray]:
     return b.astype(np.float32)
 
 
+@functools.lru_cache(maxsize=None)
+def _hot_table() -> dict:
+    with open(HOT_SETS) as f:
+        return json.load(f)
+
+
+def hot_order(cfg: LayerConfig) -> np.ndarray:
+    """Experts of a mixed-precision workload, most routed first (routes counted
+    over its full token set, ties to the lower id), from the stored table."""
+    entry = _hot_table().get(str(cfg.cid))
+    if entry is None or len(entry["order"]) != cfg.n_experts:
+        raise ValueError(f"no hot-expert table for config {cfg.cid} "
+                         f"(run tests/golden/make_hot_sets.py)")
+    return np.asarray(entry["order"], dtype=np.int64)
+
+
 def gen_tiers(cfg: LayerConfig) -> np.ndarray:
     """Per-expert precision tier [E] int32 (0 bf16, 1 int8, 2 int4).
 
-    The hottest n_bf16 experts by popularity rank are bf16, the next n_int8 are
-    int8 per-channel, the rest int4 group-128.  With a Zipf bias the rank is the
-    bias rank; without one it is an independent seeded permutation.
+    The n_bf16 most routed experts are bf16, the next n_int8 int8 per-channel,
+    the rest int4 group-128 (hot_order).
     """
     tiers = np.full(cfg.n_experts, TIER_INT4, dtype=np.int32)
     if not (cfg.n_bf16 or cfg.n_int8):
         return tiers
-    rank = _popularity_rank(cfg, _S_BIAS if cfg.zipf_bias else _S_TIERS)
-    tiers[rank <= cfg.n_bf16] = TIER_BF16
-    tiers[(rank > cfg.n_bf16) & (rank <= cfg.n_bf16 + cfg.n_int8)] = TIER_INT8
+    order = hot_order(cfg)
+    tiers[order[:cfg.n_bf16]] = TIER_BF16
+    tiers[order[cfg.n_bf16:cfg.n_bf16 + cfg.n_int8]] = TIER_INT8
     return tiers
 
 

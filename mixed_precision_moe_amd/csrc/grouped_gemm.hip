@@ -134,22 +134,18 @@ __device__ __forceinline__ bf16x8_t b_operand(const u32x4 (&b)[TierTraits<TIER>:
 // s_waitcnt immediate of gfx9: vmcnt(0), expcnt and lgkmcnt left unconstrained
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // Rows of an M-tile in the decode kernel: ROWS = 8 (MFMA rows 8..15 are
-// copies), 16 (all MFMA rows) or 32 (two MFMA row blocks per weight load),
-// chosen per forward from the mean rows per expert.  Forwards take the decode kernels up to kDecodeRowsMax mean rows
-// per expert (kDecodeRowsMaxWide for layers with many experts, see
-// plan_gemm).
+// copies), 16 (all MFMA rows), 32 or 64 (two or four MFMA row blocks per
+// weight load), chosen per forward from the mean rows per expert (plan_gemm).
 constexpr int kDecodeTileGroup = 8;   // tiles per column block kept on one XCD (grouped mapping)
-constexpr int kDecodeRowsMax = 16;
-constexpr double kDecodeRowsMaxWide = 40.0;
 // Group sums per k-group in LDS: one per MFMA row (16), or per tile row for
 // 32-row tiles (two 16-row MFMA blocks).
 __host__ __device__ constexpr int decode_rstride(int rows) { return rows > 16 ? rows : 16; }
 // A columns staged per chunk (multiples of kGroup): 4096 for 8-row tiles;
 // 1024 for 16-row and 512 for 32-row tiles, so that a chunk stays near 33 KB
-// of LDS and four blocks fit a CU; 512 for 64-row and 256 for 128-row tiles
-// (about 67 KB: two blocks per CU, as their two waves per SIMD allow)
+// of LDS and four blocks fit a CU; 512 for 64-row tiles (about 67 KB: two
+// blocks per CU, as their two waves per SIMD allow)
 __host__ __device__ constexpr int decode_chunk_cap(int rows) {
-  return rows == 8 ? 4096 : rows == 16 ? 1024 : rows == 128 ? 256 : 512;
+  return rows == 8 ? 4096 : rows == 16 ? 1024 : 512;
 }
 __host__ __device__ constexpr int decode_chunk_k(int K, int rows) {
   return K < decode_chunk_cap(rows) ? K : decode_chunk_cap(rows);
@@ -387,8 +383,8 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
   const int chunk = KSPLIT ? nb : nb * WAVES + wave;   // this wave's group of NS strips
   const int strip0 = chunk * NS;
   uint16_t* lds_a = reinterpret_cast<uint16_t*>(dyn_lds);
-  static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32 || ROWS == 64 || ROWS == 128,
-                "an M-tile is 8, 16, 32, 64 or 128 rows");
+  static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32 || ROWS == 64,
+                "an M-tile is 8, 16, 32 or 64 rows");
   constexpr int RB = ROWS > 16 ? ROWS / 16 : 1;   // 16-row MFMA blocks per tile
   float* lds_r = reinterpret_cast<float*>(dyn_lds + (size_t)ROWS * (decode_chunk_k(a.K, ROWS) + 8) * 2);
 
@@ -520,15 +516,14 @@ hipError_t launch_decode(GemmArgs a, int max_tiles, int rows, bool ksplit, hipSt
   using R16 = std::integral_constant<int, 16>;
   using R32 = std::integral_constant<int, 32>;
   using R64 = std::integral_constant<int, 64>;
-  using R128 = std::integral_constant<int, 128>;
   if (rows == 8) return ksplit ? run(std::true_type{}, R8{}) : run(std::false_type{}, R8{});
   if (rows == 16) return ksplit ? run(std::true_type{}, R16{}) : run(std::false_type{}, R16{});
   if (rows == 32) return ksplit ? run(std::true_type{}, R32{}) : run(std::false_type{}, R32{});
-  // tiles of 64 and 128 rows serve forwards with tens of routes per expert:
-  // many tiles, never split K
+  // 64-row tiles serve forwards with tens of routes per expert: many tiles,
+  // never split K.  (128-row tiles would need 128 accumulators per lane next
+  // to the weights in flight and spill.)
   if (ksplit) return hipErrorInvalidValue;
   if (rows == 64) return run(std::false_type{}, R64{});
-  if (rows == 128) return run(std::false_type{}, R128{});
   return hipErrorInvalidValue;
 }
 
@@ -592,36 +587,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }  // namespace
 
 constexpr double kDecodeRows8Max = 4.0;   // mean rows per expert up to which tiles are 8 rows
-constexpr double kDecodeRows32Min = 12.0, kDecodeRows32Max = 24.0;   // 32-row tiles in (min, max]
+constexpr double kDecodeRows16Max = 12.0;  // ... 16 rows
+constexpr double kDecodeRows32Max = 24.0;  // ... 32 rows (unless the launch splits K)
+// ... 64 rows: layers whose large-batch gate/up grid fills the 256 CUs six or
+// more times (many experts), and the others
+constexpr double kDecodeRows64MaxWide = 64.0, kDecodeRows64Max = 40.0;
 
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
   const double rows_per_expert = (double)T * L.k / L.E;
-  // The large-batch gate/up kernel runs one 256 x 256 block per CU; with few
-  // rows per expert each block is latency-bound over K.  When its blocks
-  // (one per expert and 256 columns of 2I) fill the 256 CUs six or more
-  // times, those rounds cost more than streaming an expert's weights two or
-  // three times in 16-row decode tiles (Qwen3-80B shape, 20 and 30 rows per
-  // expert: 612 -> 420 and 643 -> 532 us); elsewhere the two paths met near
-  // 16 to 32 rows, and a Zipf-skewed router favoured the large-batch path.
+  // Decode tiles stream each expert's weights once per tile with exact
+  // integer operands; the large-batch kernel (256-row tiles, fp16 MFMA) runs
+  // one 512-thread block per CU and is latency-bound over K when its tiles
+  // are far from full.  The boundaries below come from sweeps on one MI355X:
+  //   * 8-row tiles while few experts overflow them (the LDS staging then
+  //     fits any K up to 4096 in one chunk); 16-row tiles above;
+  //   * 32-row tiles (two waves per SIMD) between 12 and 24 mean rows, where
+  //     they stream most experts' weights once instead of twice: Mixtral
+  //     T = 64 277 -> 259 us, Qwen3-80B T = 1024 397 -> 371 us, Zipf-biased
+  //     Qwen3-30B T = 256 206 -> 183 us; not with the few tiles of a split-K
+  //     launch (the tiny layer: 12% slower);
+  //   * 64-row tiles above 24 mean rows: Qwen3-80B T = 2048 596 -> 520 us
+  //     (against 16-row tiles) and T = 3072 772 -> 699 us (against the large-
+  //     batch kernel), OLMoE T = 256 131 -> 117 us, Zipf-biased Qwen3-30B
+  //     T = 512 232 -> 208 us; the large-batch kernel stays ahead from
+  //     64 rows (OLMoE T = 512 160 vs 186 us, Mixtral T = 256 508 vs 611 us)
+  //     and at 80 on the many-expert layer (Qwen3-80B T = 4096 910 vs 952 us).
   const double rounds = (double)L.E * (2.0 * L.I / 256.0) / 256.0;
-  const double decode_max = rounds >= 6.0 ? kDecodeRowsMaxWide : (double)kDecodeRowsMax;
+  const double decode_max = rounds >= 6.0 ? kDecodeRows64MaxWide : kDecodeRows64Max;
   const bool decode = rows_per_expert <= decode_max;
   p.kind = decode ? kGemmDecode : kGemmPrefill;
-  // 8-row tiles while few experts overflow them (the LDS staging then fits
-  // any K up to 4096 in one chunk); 16-row tiles above; 32-row tiles (two
-  // waves per SIMD) between 12 and 24 mean rows, where they stream most
-  // experts' weights once instead of twice: Mixtral T = 64 277 -> 259 us,
-  // Qwen3-80B T = 1024 397 -> 371 us, Zipf-biased Qwen3-30B T = 256 206 ->
-  // 183 us.  At 40 rows (Qwen3-80B T = 2048) they were 4% slower than 16-row
-  // tiles, on the OLMoE shape at 16 rows 2% slower, and with the few tiles
-  // of a split-K launch (the tiny layer) 12% slower, so not there.
   int bm = 256;
   if (decode) {
-    const bool wide = !decode_split_k(L, T, 2 * L.I);   // the gate/up launch is not split-K
-    bm = rows_per_expert <= kDecodeRows8Max ? 8
-         : (wide && rows_per_expert > kDecodeRows32Min && rows_per_expert <= kDecodeRows32Max) ? 32
-         : 16;
+    const bool split = decode_split_k(L, T, 2 * L.I);   // the gate/up launch would split K
+    bm = rows_per_expert <= kDecodeRows8Max    ? 8
+         : rows_per_expert <= kDecodeRows16Max ? 16
+         : rows_per_expert <= kDecodeRows32Max ? (split ? 16 : 32)
+                                               : 64;
   }
   p.bm13 = bm;
   p.bm2 = p.bm13;

@@ -74,11 +74,12 @@ def test_layer_small_configs_full(cid):
     _run(Setup(cid))
 
 
-@pytest.mark.parametrize("T", [32, 64, 128, 512])
+@pytest.mark.parametrize("T", [32, 64, 128, 256, 512])
 def test_layer_olmoe_full(T):
     """The OLMoE-shaped layer (H 2048, E 64, top-8, I 1024): decode with 8-row
-    tiles (T 32), with 16-row tiles staged in two K-chunks (T 64, 128: 8 and
-    16 rows per expert on average), and the large-batch path (T 512)."""
+    tiles (T 32), with 16- and 32-row tiles staged in two K-chunks (T 64, 128:
+    8 and 16 rows per expert on average), with 64-row tiles (T 256: 32 rows
+    per expert, ragged), and the large-batch path (T 512)."""
     _run(Setup(6, T=T))
 
 
@@ -95,10 +96,12 @@ def test_layer_qwen80b_sweep_full(T):
     _run(Setup(4, T=T), keep=False)
 
 
-def test_layer_qwen80b_1024_full():
-    """512 experts at 20 rows per expert on average: the decode kernels with
-    32-row tiles, experts spanning up to four tiles; every output compared."""
-    _run(Setup(4, T=1024), keep=False)
+@pytest.mark.parametrize("T", [1024, 2048])
+def test_layer_qwen80b_mid_full(T):
+    """512 experts at 20 and 40 rows per expert on average: the decode kernels
+    with 32-row tiles (experts spanning up to four tiles) and with 64-row
+    tiles; every output compared."""
+    _run(Setup(4, T=T), keep=False)
 
 
 def test_layer_qwen80b_4096_tiles():
@@ -132,18 +135,20 @@ def test_layer_decode_ragged_k_chunks():
 
 @pytest.mark.parametrize("T", [65, 100, 128, 129, 200])
 def test_layer_large_batch_ragged_k(T):
-    """The large-batch kernels on a layer whose K-chunk counts are odd
-    (hidden 4352, inter 4224: 34 and 33 steps of two 64-wide chunks), all
-    routes on experts 0 (int4) and 3 (int8) at T rows each: int4 tiles of at
-    most 128 rows split K between the block's two wave rows (the down GEMM
-    with a last single step), larger ones split rows."""
+    """A layer whose K-chunk counts are odd (hidden 4352, inter 4224: 34 and
+    33 steps of two 64-wide chunks), all routes on experts 0 (int4) and 3
+    (int8) at T rows each.  Above 40 mean rows per expert (T > 80) the
+    large-batch kernels run: int4 tiles of at most 128 rows split K between
+    the block's two wave rows (the down GEMM with a last single step), larger
+    ones split rows; at T = 65 the decode kernels with 64-row tiles (a full
+    tile and a one-row tile per expert)."""
     c = dataclasses.replace(inputs.get_config(1), hidden=4352, inter=4224, n_experts=4,
                             top_k=2, max_tokens=200)
     b = np.zeros(4, np.float32)
     b[[0, 3]] = 100.0
     st = Setup(1, T=T, cfg=c, bias=b, tiers=np.array([2, 0, 2, 1]))
     layer = st.gpu_layer(experts=[0, 3])
-    assert layer.plan(T)[0] == 2
+    assert layer.plan(T) == ((2, 256) if T > 80 else (1, 64))
     _run(st, layer=layer, keep=False, runs=1)
 
 
