@@ -325,19 +325,19 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   auto read_frags = [&](int buf, int ks) {
     const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (FULL || rw.blk(rm, 4 * h)) {
+    for (int h = 0; h < 4; ++h)
+      if (FULL || rw.blk(rm, 2 * h)) {
 #pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i)
+        for (int i = 2 * h; i < 2 * h + 2; ++i)
           fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
       }
   };
   auto mfma_block = [&](int ks) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (FULL || rw.blk(rm, 4 * h)) {
+    for (int h = 0; h < 4; ++h)
+      if (FULL || rw.blk(rm, 2 * h)) {
 #pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i)
+        for (int i = 2 * h; i < 2 * h + 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
       }
@@ -562,8 +562,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // row-aware main loop for partial int4 tiles (the staged tiers always run
-  // the full tile: their row-aware variant does not fit the register budget)
+  // row-aware main loop for partial int4 tiles, skipping 32-row pairs of
+  // 16-row blocks past the tile's rows (the staged tiers always run the full
+  // tile: their row-aware variant spills 96-158 VGPRs)
   const RowWork rw{te.rows};
   const bool full = te.rows >= PBM;          // tile-uniform
   if constexpr (TIER == MOE_TIER_INT4) {
