@@ -51,16 +51,15 @@ constexpr int PBM = 256, PBN = 256, PBK = 64;
 constexpr int kPrefillThreads = 512;
 constexpr int kFragBytes = 1024;                         // one 16 x 32 fp16 operand
 constexpr int kPanelBytes = 2 * (PBM / 16) * kFragBytes; // A or B of one chunk: 32 fragments
-// LDS activation buffers of the int4 path: the chunk being read and the one
-// in flight.  Three (a DMA two chunks ahead) measured slower on every large-
-// batch workload: the workgroup fence of __syncthreads() waits for every LDS
-// DMA in flight, and a bare s_barrier with explicit waits cost more than the
-// deeper prefetch saved.
-constexpr int kAStages = 2;
+// The int4 path double-buffers its activations in steps of two 64-wide
+// chunks (two panels per buffer).  Deeper prefetch (a third buffer) measured
+// slower on every large-batch workload: the workgroup fence of
+// __syncthreads() waits for every LDS DMA in flight, and a bare s_barrier with
+// explicit waits cost more than the deeper prefetch saved.
 // 2 buffers x (activations + staged weights) = 128 KB; the int4 path uses the
 // activation half only
 constexpr size_t kPrefillLds = (size_t)2 * 2 * kPanelBytes;
-static_assert(kAStages * kPanelBytes <= (int)kPrefillLds, "int4 activation buffers fit the block's LDS");
+static_assert(4 * kPanelBytes <= (int)kPrefillLds, "int4 activation buffers fit the block's LDS");
 
 struct PrefillArgs {
   const TileEntry* tiles;
@@ -272,8 +271,6 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   const int rm = KSPLIT ? 0 : wm;                       // the wave's row half of the tile
   const bool wave_b = FULL || rw.any(rm);               // this wave needs weights
   const int K = a.K, G = K / kGroup, KC = K / PBK;
-  // steps of the loop: one chunk per wave each (KSPLIT: two chunks per block)
-  const int NJ = KSPLIT ? KC / 2 : KC;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<MOE_TIER_INT4>(a.N, K));
   const int quad = n_block / 64 + wn;                   // this wave's quad (wave-uniform)
   constexpr int kBlk = PTier<MOE_TIER_INT4>::kBlock;
@@ -281,7 +278,7 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
   // chunk values (128 B) with the 8-value slice kb in 16-byte slot kb ^ (rr/2).
   // Staging role: wave w fills tile rows 32w .. 32w+31 with 4 DMAs; lane l of
   // DMA i loads tile row 32w + 8i + l/8 into slot l%8.
-  // KSPLIT: waves 4..7 stage the odd chunk of each step, 128 bytes further on
+  // KSPLIT: waves 4..7 stage the odd chunk of each pair, 128 bytes further on
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(a.a16, a.a16_bytes);
   uint32_t avoff[4];
 #pragma unroll
@@ -297,12 +294,23 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
     const int rr = lane & 15, kb = 4 * ks + (lane >> 4);
     aread[ks] = 128u * rr + 16u * (kb ^ (rr >> 1));
   }
-  auto As = [&](int buf) { return lds + buf * kPanelBytes; };
+  // A step of the loop covers kStep 64-wide chunks per wave (half c of the
+  // step), each with its own 32 KB panel; the activations are double-buffered
+  // by step.  Full tiles take one chunk per step; partial tiles (latency-bound
+  // over K: few rows, or KSPLIT) two, so one barrier and one DMA wait cover
+  // 128 k per wave (Mixtral-shaped full tiles measured 3% slower with two,
+  // OLMoE T = 512 7% and Mixtral T = 256 8% faster).
+  constexpr int kStep = FULL ? 1 : 2;
+  auto As = [&](int buf, int c) { return lds + (kStep * buf + c) * kPanelBytes; };
   const Int4Consts k4 = fp16_int4_consts();
-  // K chunk of this wave in loop step j
-  auto chunk_of = [&](int j) { return KSPLIT ? 2 * j + wm : j; };
+  // K chunk of this wave in half c of step j (KSPLIT: wave row h takes chunks
+  // 2 kStep j + 2c + h), clamped into K: a clamped chunk only feeds a skipped
+  // half or a prefetch that is never used
+  auto chunk_of = [&](int j, int c) {
+    return min(KSPLIT ? 2 * kStep * j + 2 * c + wm : kStep * j + c, KC - 1);
+  };
+  const int NJ = KSPLIT ? (KC + 2 * kStep - 1) / (2 * kStep) : KC / kStep;   // KC is even
 
-  // weights of chunk c travel in register slot c % 2, two chunks ahead
   BDirect braw0, braw1;
   auto load_b = [&](int kc, BDirect& raw) {
     if (!wave_b) return;
@@ -311,19 +319,24 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
     for (int j = 0; j < 4; ++j) raw.w[j] = buffer_load8(rsrc, 16 * lane + 1024 * j, block + 8 * (kc & 1));
     raw.scale = buffer_load8(rsrc, 8 * (lane & 15), block + 4096u);
   };
-  // activations of step j (KSPLIT: chunks 2j and 2j + 1)
+  // activations of step j: half c holds chunk kStep j + c (KSPLIT: chunks
+  // 2 kStep j + 2c and the one after, by wave rows 0 and 1)
   auto dma_a = [&](int j, int buf) {
     if (!FULL && !rw.dma(KSPLIT ? (wave & 3) : wave)) return;
-    lds_u8* dst = As(buf) + 4 * wave * 1024;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
-                                               2u * PBK * (KSPLIT ? 2 * j : j), 0, 0);
+    for (int c = 0; c < kStep; ++c) {
+      const int cc = KSPLIT ? min(2 * kStep * j + 2 * c, KC - 2) : kStep * j + c;
+      lds_u8* dst = As(buf, c) + 4 * wave * 1024;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(dst + i * 1024), 16, avoff[i],
+                                                 2u * PBK * cc, 0, 0);
+    }
   };
 
   f16x8_t fa[2][8], fb[2][4];
-  auto read_frags = [&](int buf, int ks) {
-    const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
+  auto read_frags = [&](int buf, int c, int ks) {
+    const lds_u8* Aw = As(buf, c) + 8 * wm * 2048 + aread[ks];
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       if (FULL || rw.blk(rm, 2 * h)) {
@@ -342,43 +355,60 @@ __device__ __forceinline__ void prefill_mainloop_direct(const PrefillArgs& a, co
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
       }
   };
-
-  // One step: the activations kAStages - 1 steps ahead stream into a free
-  // LDS buffer by DMA; this chunk's weights (loaded two chunks ago) are
-  // dequantized into MFMA operands and their register slot refilled with the
-  // weights two chunks ahead.  Prefetch indices are clamped at the end of K (a
-  // repeated load of the last chunk, never used), so the body has no branches
-  // and the compiler's load waits stay exact.  KC is even (K is a multiple of
-  // 128): unrolled by two, each register slot keeps its role.  Before the
-  // chunk's barrier each wave waits for its DMA of the next chunk; what it
-  // issued after that DMA (weights, later DMAs) may stay in flight: 5 loads per
-  // chunk of weights, 4 per chunk of activations.
-  constexpr int kAhead = kAStages - 1;
-  constexpr int kWaitNext = wait_vmcnt(5 + (kAhead - 1) * 9);
-  auto step = [&](int j, BDirect& raw) {
-    const int buf = j % kAStages;
-    dma_a(min(j + kAhead, NJ - 1), (j + kAhead) % kAStages);
+  // one chunk of a step: dequantize its weights (loaded two chunks ago),
+  // refill their register slot with chunk `ahead`, then the 2 x 8 x 4 MFMAs
+  auto chunk = [&](int buf, int c, int ahead, BDirect& raw) {
     if (wave_b) dequant_b(raw, fb, k4);
-    load_b(chunk_of(min(j + 2, NJ - 1)), raw);
-    read_frags(buf, 0);
-    read_frags(buf, 1);
+    load_b(ahead, raw);
+    read_frags(buf, c, 0);
+    read_frags(buf, c, 1);
     mfma_block(0);
     mfma_block(1);
-    __builtin_amdgcn_s_waitcnt(kWaitNext);
-    __syncthreads();
   };
-  load_b(chunk_of(0), braw0);
-  load_b(chunk_of(min(1, NJ - 1)), braw1);
-#pragma unroll
-  for (int c = 0; c < kAhead; ++c) dma_a(min(c, NJ - 1), c);
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt((kAhead - 1) * 4));   // step 0 is in LDS
-  __syncthreads();
-  int j = 0;
-  for (; j + 2 <= NJ; j += 2) {
-    step(j, braw0);
-    step(j + 1, braw1);
+
+  // Each step first streams the next step's activations into the other
+  // buffer by DMA (4 loads per chunk and lane).  Prefetch indices are clamped
+  // at the end of K (repeated loads, never used), so the body has no branches
+  // and the compiler's load waits stay exact.  Before the barrier each wave
+  // waits for its DMA of the next step; the weight loads it issued after that
+  // DMA (5 per chunk: two chunks ahead) stay in flight.
+  constexpr int kWaitNext = wait_vmcnt(5 * kStep);
+  if constexpr (kStep == 1) {
+    // slots alternate by chunk parity (unrolled by two, KC even)
+    load_b(chunk_of(0, 0), braw0);
+    load_b(chunk_of(min(1, NJ - 1), 0), braw1);
+    dma_a(0, 0);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __syncthreads();
+    auto step = [&](int j, BDirect& raw) {
+      const int buf = j & 1;
+      dma_a(min(j + 1, NJ - 1), buf ^ 1);
+      chunk(buf, 0, chunk_of(min(j + 2, NJ - 1), 0), raw);
+      __builtin_amdgcn_s_waitcnt(kWaitNext);
+      __syncthreads();
+    };
+    for (int j = 0; j < NJ; j += 2) {
+      step(j, braw0);
+      step(j + 1, braw1);
+    }
+  } else {
+    // slot c holds half c, one step ahead
+    load_b(chunk_of(0, 0), braw0);
+    load_b(chunk_of(0, 1), braw1);
+    dma_a(0, 0);
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __syncthreads();
+    for (int j = 0; j < NJ; ++j) {
+      const int buf = j & 1;
+      const int jn = min(j + 1, NJ - 1);
+      dma_a(jn, buf ^ 1);
+      chunk(buf, 0, chunk_of(jn, 0), braw0);
+      // KSPLIT with K / 128 odd: the last step has one chunk per wave row
+      if (!KSPLIT || 4 * j + 2 < KC) chunk(buf, 1, chunk_of(jn, 1), braw1);
+      __builtin_amdgcn_s_waitcnt(kWaitNext);
+      __syncthreads();
+    }
   }
-  if (j < NJ) step(j, braw0);   // KSPLIT with K / 128 odd: one step left
   if constexpr (KSPLIT) {
     // the odd chunks' sums (wave row 1) join the even chunks' (wave row 0) in
     // LDS, which the loop's last barrier has freed; only 16-row blocks with a
