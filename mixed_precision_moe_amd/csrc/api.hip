@@ -613,8 +613,8 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
   }
   if (e != hipSuccess) return check_hip(e, "down GEMM launch");
   st.rec(5);
-  e = launch_combine(at<float>(ws, p.rows), at<int32_t>(ws, p.pos), at<int32_t>(ws, p.ids),
-                     wave.slot_map, T, L->H, L->k, y, y_dtype, accumulate, s);
+  e = launch_combine(at<float>(ws, p.rows), at<int32_t>(ws, p.ids), wave.slot_map, T, L->H, L->k,
+                     y, y_dtype, accumulate, s);
   if (e != hipSuccess) return check_hip(e, "combine launch");
   st.rec(6);
   return MOE_OK;

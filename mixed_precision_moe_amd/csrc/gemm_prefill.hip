@@ -73,7 +73,7 @@ struct PrefillArgs {
   uint16_t* act16;           // gate/up output [T*k, I] fp16 (bf16-rounded values)
   int I;
   const float* topk_w;       // down epilogue
-  float* rows;               // [T*k, H]
+  float* rows;               // [T*k, H] fp32, by route id
   int xcd_group;             // > 0: launch-order groups of this many blocks stay on one XCD
 };
 
@@ -633,9 +633,9 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
       for (int e = 0; e < 4; ++e) {
         const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
         if (m < te.rows) {
-          const int pos = te.row_start + m;
-          const float wgt = a.topk_w[a.sorted[pos]];
-          float* out = a.rows + (size_t)pos * a.N + col0 + (lane & 15);
+          const int r = a.sorted[te.row_start + m];   // route id t k + j: rows are in route order
+          const float wgt = a.topk_w[r];
+          float* out = a.rows + (size_t)r * a.N + col0 + (lane & 15);
 #pragma unroll
           for (int j = 0; j < 4; ++j) out[16 * j] = wgt * acc[i][j][e];
         }

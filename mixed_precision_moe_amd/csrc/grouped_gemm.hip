@@ -57,7 +57,7 @@ struct GemmArgs {
   int I;
   // down epilogue
   const float* topk_w;       // [T*k] routing weights by route id
-  float* rows;               // [T*k, H] fp32, grouped order
+  float* rows;               // [T*k, H] fp32, by route id (t k + j)
   int tile_group;            // non-zero and ntiles[1] set: kDecodeTileGroup consecutive tiles of one column block share an XCD
 };
 
@@ -458,9 +458,9 @@ void gemm_decode_kernel(GemmArgs a, int blocks_per_tile) {
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * rb + 4 * (lane >> 4) + i;
         if (m < te.rows) {
-          const int pos = te.row_start + m;
-          const float wgt = a.topk_w[a.sorted[pos]];
-          float* out = a.rows + (size_t)pos * a.N + 16 * strip0 + (lane & 15);
+          const int r = a.sorted[te.row_start + m];   // route id t k + j: rows are in route order
+          const float wgt = a.topk_w[r];
+          float* out = a.rows + (size_t)r * a.N + 16 * strip0 + (lane & 15);
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) out[16 * ns] = wgt * acc[rb * NS + ns][i];
         }
@@ -536,31 +536,31 @@ bool decode_split_k(const Layer& L, int T, int N) {
 }
 
 
-// Sum of a token's k weighted rows in ascending expert order, fp32.  With a
-// slot map (wave mode) routes of experts mapped to the sentinel are skipped,
-// and with ACC the sum is added to y (fp32 only).  KMAX >= k is the
-// compile-time bound of the route loops: every row load is issued before the
-// first add (loads past k repeat route k-1's row and are not added).
+// Sum of a token's k weighted rows in ascending expert order, fp32.  The down
+// GEMMs write the rows by route id (t k + j), so a token's k rows are
+// contiguous and slot j is expert ids[t k + j] (ids ascending).  With a slot
+// map (wave mode) routes of experts mapped to the sentinel are skipped, and
+// with ACC the sum is added to y (fp32 only).  KMAX >= k is the compile-time
+// bound of the route loops: every row load is issued before the first add
+// (loads past k repeat route k-1's row and are not added).
 template <bool BF16_OUT, bool ACC, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ rows,
-                                                      const int32_t* __restrict__ pos,
                                                       const int32_t* __restrict__ ids,
                                                       const int32_t* __restrict__ slot_map, int T,
                                                       int H, int k, void* __restrict__ y) {
   const int t = blockIdx.y;
   const int h4 = (blockIdx.x * 256 + threadIdx.x) * 4;
-  // lane j of each wave loads route j's position (one vector load), then
-  // every lane takes all of them with readlane (k is block-uniform)
-  const int lane = threadIdx.x & 63;
-  const int jl = min(lane, k - 1);
-  const int my_pos = pos[t * k + jl];
   uint64_t keep = ~0ull;
-  if (slot_map) keep = __ballot(slot_map[ids[t * k + jl]] >= 0);   // wave mode
+  if (slot_map) {   // wave mode: lane j tests route j's expert, one ballot
+    const int jl = min((int)(threadIdx.x & 63), k - 1);
+    keep = __ballot(slot_map[ids[t * k + jl]] >= 0);
+  }
   if (h4 >= H) return;   // after the wave-wide loads above
+  const float* rt = rows + (size_t)t * k * H + h4;
   float4 v[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j)
-    v[j] = *reinterpret_cast<const float4*>(rows + (size_t)__builtin_amdgcn_readlane(my_pos, j) * H + h4);
+    v[j] = *reinterpret_cast<const float4*>(rt + (size_t)min(j, k - 1) * H);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
@@ -677,20 +677,19 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   return launch_decode<4, false>(a, max_tiles, gp.bm2, ks, s, KernelTimer{nullptr, nullptr});
 }
 
-hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
-                          const int32_t* slot_map, int T, int H, int k, void* y, int y_dtype,
-                          bool accumulate, hipStream_t s) {
+hipError_t launch_combine(const float* rows, const int32_t* ids, const int32_t* slot_map, int T,
+                          int H, int k, void* y, int y_dtype, bool accumulate, hipStream_t s) {
   const dim3 grid((H / 4 + 255) / 256, T);
   auto run = [&](auto kmax) {
     constexpr int KM = decltype(kmax)::value;
     if (y_dtype == MOE_DTYPE_BF16)
-      hipLaunchKernelGGL((combine_kernel<true, false, KM>), grid, dim3(256), 0, s, rows, pos, ids,
+      hipLaunchKernelGGL((combine_kernel<true, false, KM>), grid, dim3(256), 0, s, rows, ids,
                          slot_map, T, H, k, y);
     else if (accumulate)
-      hipLaunchKernelGGL((combine_kernel<false, true, KM>), grid, dim3(256), 0, s, rows, pos, ids,
+      hipLaunchKernelGGL((combine_kernel<false, true, KM>), grid, dim3(256), 0, s, rows, ids,
                          slot_map, T, H, k, y);
     else
-      hipLaunchKernelGGL((combine_kernel<false, false, KM>), grid, dim3(256), 0, s, rows, pos, ids,
+      hipLaunchKernelGGL((combine_kernel<false, false, KM>), grid, dim3(256), 0, s, rows, ids,
                          slot_map, T, H, k, y);
     return hipGetLastError();
   };

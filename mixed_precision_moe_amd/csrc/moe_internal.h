@@ -207,10 +207,10 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream
 hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
                           uint16_t* act16, const float* topk_w, float* rows, hipStream_t s, KernelTimer kt = KernelTimer{nullptr, nullptr});
-// y[t] (=|+=) sum over the token's routes in ascending expert order; with a
-// slot map, routes whose expert maps to the sentinel are skipped.
-hipError_t launch_combine(const float* rows, const int32_t* pos, const int32_t* ids,
-                          const int32_t* slot_map, int T, int H, int k, void* y, int y_dtype,
-                          bool accumulate, hipStream_t s);
+// y[t] (=|+=) sum over the token's routes in ascending expert order (rows
+// [T k, H] by route id); with a slot map, routes whose expert maps to the
+// sentinel are skipped.
+hipError_t launch_combine(const float* rows, const int32_t* ids, const int32_t* slot_map, int T,
+                          int H, int k, void* y, int y_dtype, bool accumulate, hipStream_t s);
 
 }  // namespace moe
