@@ -395,15 +395,18 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   int* off = cnt + 16 * E;        // [E+1] exclusive scan of totals
   int* scan = off + E + 1;        // [1024] scan scratch
   int* hist = off + E + 1 + 1024;  // [kMaxTileRows] tile-ordering histogram
+  int* eid = hist + kMaxTileRows;  // [T k] the routes' experts (clamped)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = (T + 15) / 16;
   const int tb = min(T, wave * chunk), te = min(T, tb + chunk);
   const TileSource src = tile_source(table, wmap, E);
 
+  // every route's expert into LDS with one coalesced pass, so the walks
+  // below (one token after another) read LDS instead of memory
+  for (int r = tid; r < T * k; r += 1024) eid[r] = min(max(ids[r], 0), E - 1);
   for (int i = tid; i < 16 * E; i += 1024) cnt[i] = 0;
   __syncthreads();
-  for (int r = tb * k + lane; r < te * k; r += 64)
-    atomicAdd(&cnt[wave * E + min(max(ids[r], 0), E - 1)], 1);
+  for (int r = tb * k + lane; r < te * k; r += 64) atomicAdd(&cnt[wave * E + eid[r]], 1);
   __syncthreads();
 
   // per expert: prefix over the 16 chunks; total -> off[e]
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   for (int t = tb; t < te; ++t) {
     if (lane < k) {
       const int r = t * k + lane;
-      const int e = min(max(ids[r], 0), E - 1);
+      const int e = eid[r];
       const int p = off[e] + cnt[wave * E + e];
       cnt[wave * E + e] += 1;
       sorted[p] = r;
@@ -454,14 +457,19 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ chunk_counts) {
   __shared__ int cnt[4][kMaxExperts];
   __shared__ int rk[kPermChunk * kMaxTopK];
+  __shared__ int eid[kPermChunk * kMaxTopK];   // the block's routes' experts (clamped)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * kPermChunk;
+  const int nr = (min(T, t0 + kPermChunk) - t0) * k;   // routes of this block
+  // one coalesced pass brings the block's experts into LDS: the walk below
+  // (one token after another) then reads LDS instead of memory
+  for (int i = tid; i < nr; i += 256) eid[i] = min(max(ids[(size_t)t0 * k + i], 0), E - 1);
   for (int e = tid; e < 4 * kMaxExperts; e += 256) (&cnt[0][0])[e] = 0;
   __syncthreads();
   const int tb = min(T, t0 + 64 * wave), te = min(T, tb + 64);
   for (int t = tb; t < te; ++t) {
     if (lane < k) {
-      const int e = min(max(ids[t * k + lane], 0), E - 1);
+      const int e = eid[(t - t0) * k + lane];
       rk[(t - t0) * k + lane] = cnt[wave][e];
       cnt[wave][e] += 1;
     }
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(256) void permute_rank_kernel(const int32_t* __rest
   __syncthreads();
   for (int i = lane; i < (te - tb) * k; i += 64) {
     const int r = tb * k + i;
-    const int e = min(max(ids[r], 0), E - 1);
+    const int e = eid[r - t0 * k];
     int before = 0;
     for (int w = 0; w < wave; ++w) before += cnt[w][e];
     rank[r] = rk[r - t0 * k] + before;
@@ -634,11 +642,13 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
                        tiles2, ntiles2);
     return hipGetLastError();
   }
-  const size_t lds = sizeof(int) * (17 * (size_t)E + 1025 + kMaxTileRows);
-  // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB)
+  const size_t lds = sizeof(int) * (17 * (size_t)E + 1025 + kMaxTileRows + (size_t)T * k);
+  // > 64 KB of LDS needs an opt-in (gfx950 has 160 KB; the largest case,
+  // 1024 experts and 1024 tokens at top-16, takes 137 KB)
   static DeviceOnce lds_opt_in;
-  const hipError_t ea = ensure_dynamic_lds(lds_opt_in, reinterpret_cast<const void*>(permute_kernel),
-                                           (int)(sizeof(int) * (17 * kMaxExperts + 1025 + kMaxTileRows)));
+  const hipError_t ea = ensure_dynamic_lds(
+      lds_opt_in, reinterpret_cast<const void*>(permute_kernel),
+      (int)(sizeof(int) * (17 * kMaxExperts + 1025 + kMaxTileRows + kPermSmallT * kMaxTopK)));
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, wave, hotness, ids, T, k, E, offsets, sorted,
                      pos, tiles13, ntiles13, bm13, tiles2, ntiles2);
