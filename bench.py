@@ -377,7 +377,7 @@ def measure(cfg, T, steps, warmup, args, dev):
     ws = torch.empty(layers[0].workspace_size(T), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     fwd = [L.bind_forward(x, wr, bias, y, workspace=ws, stream=stream) for L in layers]
-    path, tile_rows = layers[0].plan(T)
+    (path, tile_rows), (path2, tile_rows2) = layers[0].plan_gemms(T)
 
     # routing (for the algorithmic byte/flop counts): outside the timed region
     route = layers[0].route(x, wr, bias)
@@ -472,6 +472,9 @@ def measure(cfg, T, steps, warmup, args, dev):
         "gemm_path": {1: "few routes per expert (weight streaming)",
                       2: "many routes per expert (fp16 MFMA)"}.get(path, str(path)),
         "tile_rows": tile_rows,
+        "down_gemm_path": {1: "few routes per expert (weight streaming)",
+                           2: "many routes per expert (fp16 MFMA)"}.get(path2, str(path2)),
+        "down_tile_rows": tile_rows2,
         "weight_copies_rotated": R, "output": args.out_dtype,
         "launch": launch, "ms_per_step_host_launch": round(eager_ms / steps, 4),
         "layer_roofline_frac": round(layer_roof_s / (ms_per_step / 1000.0), 4),

@@ -237,16 +237,22 @@ int moe_layer_set_router_mode(moe_layer_t layer, int32_t mode);
  * stream that has work using the layer. */
 int moe_layer_destroy(moe_layer_t layer);
 
-/* Which grouped-GEMM family and M-tile height a forward of T tokens takes
- * (a diagnostic for callers and tests; it never changes results).
- *   path       1: few routes per expert (weight streaming, exact integer MFMA
- *              operands); 2: many routes per expert (fp16 MFMA, dequantized
- *              weights rounded once to fp16).
- *   tile_rows  routes per M-tile of both grouped GEMMs: an expert's routes, in
+/* Which grouped-GEMM family and M-tile height each GEMM of a forward of T
+ * tokens takes (a diagnostic for callers and tests).
+ *   path       gate/up GEMM: 1, few routes per expert (weight streaming, exact
+ *              integer MFMA operands); 2, many routes per expert (fp16 MFMA,
+ *              dequantized weights rounded once to fp16).
+ *   tile_rows  routes per M-tile of the gate/up GEMM: an expert's routes, in
  *              grouped order, are cut into tiles of this many (the last one
  *              ragged).
- * Host only; MOE_EINVAL for null pointers, MOE_ESHAPE for T outside [0, 2^24]. */
-int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_rows);
+ *   down_path, down_tile_rows  the same for the down GEMM (either may be
+ *              NULL).  The two differ in one case: tens of routes per expert
+ *              on layers with many experts, where a path-2 gate/up GEMM feeds
+ *              a path-1 down GEMM.
+ * Host only; MOE_EINVAL for null path or tile_rows, MOE_ESHAPE for T outside
+ * [0, 2^24]. */
+int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_rows,
+                   int32_t* down_path, int32_t* down_tile_rows);
 
 /* Bytes of device workspace a route or forward call with T tokens needs.
  * The workspace is scratch: no state is kept in it between calls, except that
@@ -288,8 +294,8 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
  *     aligned.  x and y must be 16-byte aligned.
  * T may be 0 (nothing is enqueued).  Calls that share a workspace must be
  * ordered on one stream.
- * When a call takes the many-routes-per-expert path (moe_layer_plan path 2),
- * T*H*2 and T*k*I*2 must each stay below 4 GiB (its kernels address these
+ * When either GEMM takes the many-routes-per-expert path (moe_layer_plan path
+ * 2), T*H*2 and T*k*I*2 must each stay below 4 GiB (its kernels address these
  * 16-bit activation arrays with 32-bit offsets): MOE_ESHAPE otherwise, before
  * any work is enqueued; split such a batch into several calls. */
 int moe_layer_forward(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,

@@ -87,7 +87,8 @@ def load() -> ctypes.CDLL:
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (ctypes.c_int, []),
         "moe_unpack_codes": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, vp, sz, i64, i64, vp, vp]),
-        "moe_layer_plan": (ctypes.c_int, [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+        "moe_layer_plan": (ctypes.c_int, [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                          ctypes.POINTER(i32), ctypes.POINTER(i32)]),
         "moe_layer_forward_noalloc": (ctypes.c_int, [vp, vp, vp, vp, i32, vp, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():

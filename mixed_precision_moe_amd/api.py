@@ -145,13 +145,18 @@ class Layer:
     def workspace_size(self, T: int) -> int:
         return int(self._lib.moe_workspace_size(self._h, int(T)))
 
+    def plan_gemms(self, T: int) -> Tuple[Tuple[int, int], Tuple[int, int]]:
+        """((path, tile_rows) of the gate/up GEMM, (path, tile_rows) of the down
+        GEMM) for a forward of T tokens: path 1 = few routes per expert (weight
+        streaming), 2 = many (fp16 MFMA); routes per M-tile."""
+        p13, r13, p2, r2 = (ctypes.c_int32() for _ in range(4))
+        check(self._lib.moe_layer_plan(self._h, int(T), ctypes.byref(p13), ctypes.byref(r13),
+                                       ctypes.byref(p2), ctypes.byref(r2)), "moe_layer_plan")
+        return (p13.value, r13.value), (p2.value, r2.value)
+
     def plan(self, T: int) -> Tuple[int, int]:
-        """(path, tile_rows) a forward of T tokens takes: path 1 = few routes
-        per expert (weight streaming), 2 = many (fp16 MFMA); routes per M-tile."""
-        path, rows = ctypes.c_int32(), ctypes.c_int32()
-        check(self._lib.moe_layer_plan(self._h, int(T), ctypes.byref(path), ctypes.byref(rows)),
-              "moe_layer_plan")
-        return path.value, rows.value
+        """(path, tile_rows) of the gate/up GEMM (plan_gemms has both GEMMs)."""
+        return self.plan_gemms(T)[0]
 
     def workspace(self, T: int, device) -> torch.Tensor:
         """A cached workspace tensor large enough for T tokens (allocated by torch)."""

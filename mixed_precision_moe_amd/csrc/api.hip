@@ -422,7 +422,8 @@ int moe_layer_destroy(moe_layer_t layer) {
   return rc ? rc : rc2 ? rc2 : rc3;
 }
 
-int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_rows) {
+int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_rows,
+                   int32_t* down_path, int32_t* down_tile_rows) {
   g_err[0] = 0;
   const Layer* L = reinterpret_cast<const Layer*>(layer);
   if (!L || !path || !tile_rows) return set_error(MOE_EINVAL, "null pointer");
@@ -430,6 +431,8 @@ int moe_layer_plan(moe_layer_t layer, int32_t T, int32_t* path, int32_t* tile_ro
   const GemmPlan gp = plan_gemm(*L, T);
   *path = gp.kind;
   *tile_rows = gp.bm13;
+  if (down_path) *down_path = gp.kind2;
+  if (down_tile_rows) *down_tile_rows = gp.bm2;
   return MOE_OK;
 }
 
@@ -483,7 +486,7 @@ int check_common(const Layer* L, const uint16_t* x, const uint16_t* wr, int32_t 
   // The large-batch GEMMs read their 16-bit activations (x [T, H] and the
   // SwiGLU output [T k, I]) through 32-bit buffer records and offsets, so each
   // array must stay below 4 GiB; larger batches are split by the caller.
-  if (gemm && gp->kind == kGemmPrefill &&
+  if (gemm && (gp->kind == kGemmPrefill || gp->kind2 == kGemmPrefill) &&
       ((uint64_t)T * L->H * 2 > 0xffffffffull || (uint64_t)T * L->k * L->I * 2 > 0xffffffffull))
     return set_error(MOE_ESHAPE,
                      "%d tokens: the large-batch path needs T*H*2 and T*k*I*2 below 4 GiB "
@@ -577,7 +580,11 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
   if (!y || !aligned(y, 16)) return set_error(MOE_EINVAL, "y must be non-null and 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const Stages st{L, s, true};
-  const bool prefill = gp.kind == kGemmPrefill;
+  const bool prefill = gp.kind == kGemmPrefill;     // the gate/up GEMM's family
+  const bool prefill2 = gp.kind2 == kGemmPrefill;   // the down GEMM's
+  // a large-batch down GEMM reads fp16 activations, which only the
+  // large-batch gate/up GEMM writes (plan_gemm never pairs it otherwise)
+  if (prefill2 && !prefill) return set_error(MOE_EINVAL, "unsupported GEMM plan");
   // the hotness trace counts each layer call once: a plain forward, or the
   // first wave of a layer call (the one that does not accumulate)
   const Hotness hotness{accumulate ? nullptr : L->hot, L->hot_decay};
@@ -593,7 +600,8 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
     if (e == hipSuccess)
       e = launch_prefill(true, *L, T, at<uint16_t>(ws, p.x16), at<int32_t>(ws, p.sorted),
                          at<TileEntry>(ws, p.tiles13), at<int32_t>(ws, p.ntiles13), p.max_tiles13,
-                         at<uint16_t>(ws, p.act), nullptr, nullptr, s, st.gate_up_timer());
+                         at<uint16_t>(ws, p.act), prefill2 ? nullptr : at<float>(ws, p.r2), nullptr,
+                         nullptr, s, st.gate_up_timer());
   } else {
     e = launch_gemm13(*L, gp, T, x, at<int32_t>(ws, p.sorted), at<TileEntry>(ws, p.tiles13),
                       at<int32_t>(ws, p.ntiles13), p.max_tiles13, at<float>(ws, p.r13),
@@ -601,10 +609,10 @@ int forward_impl(const Layer* L, WaveMap wave, bool accumulate, const uint16_t* 
   }
   if (e != hipSuccess) return check_hip(e, "gate/up GEMM launch");
   st.rec(4);
-  if (prefill) {
+  if (prefill2) {
     e = launch_prefill(false, *L, T, at<uint16_t>(ws, p.act), at<int32_t>(ws, p.sorted),
                        at<TileEntry>(ws, p.tiles2), at<int32_t>(ws, p.ntiles2), p.max_tiles2,
-                       nullptr, at<float>(ws, p.weights), at<float>(ws, p.rows), s);
+                       nullptr, nullptr, at<float>(ws, p.weights), at<float>(ws, p.rows), s);
   } else {
     e = launch_gemm2(*L, gp, T, at<uint16_t>(ws, p.act), at<int32_t>(ws, p.sorted),
                      at<float>(ws, p.weights), at<TileEntry>(ws, p.tiles2),

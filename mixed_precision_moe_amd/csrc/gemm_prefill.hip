@@ -70,7 +70,9 @@ struct PrefillArgs {
   const int32_t* sorted;
   int top_k;
   int K, N;
-  uint16_t* act16;           // gate/up output [T*k, I] fp16 (bf16-rounded values)
+  uint16_t* act16;           // gate/up output [T*k, I]: fp16 re-encodings of bf16-rounded
+                             // values, or the bf16 values themselves (BF16_OUT)
+  float* r2;                 // BF16_OUT: each row's sum of every 32 activation columns [T*k, I/32]
   int I;
   const float* topk_w;       // down epilogue
   float* rows;               // [T*k, H] fp32, by route id
@@ -580,8 +582,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_as_f16(float v) {
 }
 
 // One tile of one tier: accumulate, then the epilogue (SwiGLU -> fp16
-// activations for gate/up; routing weight -> fp32 rows for down).
-template <int TIER, bool GATE_UP>
+// activations for gate/up, or for the decode down GEMM (BF16_OUT) bf16 ones
+// and their 32-column row sums; routing weight -> fp32 rows for down).
+// BF16_OUT is a template argument, so each kernel carries one epilogue.  The
+// row sums go through a per-wave LDS scratch, not cross-lane shuffles: with
+// shuffles the compiler copied the epilogue and main loops per tier and tile
+// kind, and the kernel, 2.5 times the code, ran 20% slower.
+template <int TIER, bool GATE_UP, bool BF16_OUT>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEntry& te,
                                              const uint8_t* blob, const int (&arow)[4],
                                              int n_block, lds_u8* plds) {
@@ -611,20 +618,59 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
   }
   const int col0 = n_block + 64 * wn;      // first packed column of this wave (one quad)
   if constexpr (GATE_UP) {
-    // strips 0, 1 of the quad are gate, 2, 3 the matching up columns
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int icol = 32 * (col0 / 64) + 16 * half + (lane & 15);
+    // strips 0, 1 of the quad are gate, 2, 3 the matching up columns: the
+    // wave's quad is activation columns 32 c .. 32 c + 31, c = col0 / 64
+    const int c = col0 / 64;
+    if constexpr (BF16_OUT) {
+      // Every main loop ends at a block barrier past its last LDS read, so
+      // the wave owns 16 KB of LDS here: for the split-K tiles, the part its
+      // own reduction has just read (wave row 1 has left).  Lane (r, col)
+      // leaves its pair of bf16 values' sum for tile row r of the wave's 128;
+      // each lane then adds the 16 of two rows in column order.
+      lds_f32* sc = reinterpret_cast<lds_f32*>(plds + wn * 32768 + wm * 16384);
+      constexpr int kStride = 17;   // floats per row: the column writes spread over the banks
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
-          if (m < te.rows) {
-            const float g = acc[i][half][e], up = acc[i][half + 2][e];
-            a.act16[(size_t)(te.row_start + m) * a.I + icol] = f32_to_bf16_as_f16(silu_f32(g) * up);
+          const int ml = 16 * i + 4 * (lane >> 4) + e, m = 128 * wm + ml;
+          float rs = 0.0f;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const uint32_t b16 = f32_to_bf16_rne(silu_f32(acc[i][half][e]) * acc[i][half + 2][e]);
+            if (m < te.rows)
+              a.act16[(size_t)(te.row_start + m) * a.I + 32 * c + 16 * half + (lane & 15)] = (uint16_t)b16;
+            rs += bf16_to_f32(b16);
           }
+          sc[ml * kStride + (lane & 15)] = rs;
         }
+      // one wave's LDS operations complete in order; this keeps the compiler
+      // from moving the reads above the writes
+      __asm__ volatile("" ::: "memory");
+      const int P = a.I / 32;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ml = lane + 64 * h, m = 128 * wm + ml;
+        float r = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) r += sc[ml * kStride + j];
+        if (m < te.rows) a.r2[(size_t)(te.row_start + m) * P + c] = r;
+      }
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int icol = 32 * c + 16 * half + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 128 * wm + 16 * i + 4 * (lane >> 4) + e;
+            if (m < te.rows) {
+              const float g = acc[i][half][e], up = acc[i][half + 2][e];
+              a.act16[(size_t)(te.row_start + m) * a.I + icol] = f32_to_bf16_as_f16(silu_f32(g) * up);
+            }
+          }
+      }
     }
   } else {
 #pragma unroll
@@ -645,7 +691,7 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
 
 constexpr int kXcdGroupMinK = 4096;
 
-template <bool GATE_UP>
+template <bool GATE_UP, bool BF16_OUT>
 __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t plds[];
   // Column blocks of one M-tile are adjacent in launch order, so the blocks
@@ -690,9 +736,9 @@ __global__ __launch_bounds__(kPrefillThreads, 1) void gemm_prefill_kernel(Prefil
   const uint8_t* blob = te.w;
   lds_u8* lds = (lds_u8*)plds;
   switch (te.tier) {
-    case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP>(a, te, blob, arow, n_block, lds); break;
-    case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP>(a, te, blob, arow, n_block, lds); break;
-    default: prefill_body<MOE_TIER_BF16, GATE_UP>(a, te, blob, arow, n_block, lds); break;
+    case MOE_TIER_INT4: prefill_body<MOE_TIER_INT4, GATE_UP, BF16_OUT>(a, te, blob, arow, n_block, lds); break;
+    case MOE_TIER_INT8: prefill_body<MOE_TIER_INT8, GATE_UP, BF16_OUT>(a, te, blob, arow, n_block, lds); break;
+    default: prefill_body<MOE_TIER_BF16, GATE_UP, BF16_OUT>(a, te, blob, arow, n_block, lds); break;
   }
 }
 
@@ -719,9 +765,10 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream
 
 hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
-                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s,
-                          KernelTimer kt) {
+                          uint16_t* act16, float* r2, const float* topk_w, float* rows,
+                          hipStream_t s, KernelTimer kt) {
   PrefillArgs a{};
+  a.r2 = gate_up ? r2 : nullptr;
   a.tiles = tiles;
   a.ntiles = ntiles;
   a.max_tiles = max_tiles;
@@ -735,10 +782,12 @@ hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a
   a.I = L.I;
   a.topk_w = topk_w;
   a.rows = rows;
-  static DeviceOnce lds_opt_in[2];
-  const void* kern = gate_up ? reinterpret_cast<const void*>(gemm_prefill_kernel<true>)
-                             : reinterpret_cast<const void*>(gemm_prefill_kernel<false>);
-  const hipError_t ea = ensure_dynamic_lds(lds_opt_in[gate_up ? 1 : 0], kern, (int)kPrefillLds);
+  static DeviceOnce lds_opt_in[3];
+  const int variant = !gate_up ? 0 : a.r2 ? 2 : 1;
+  const void* kern = variant == 0 ? reinterpret_cast<const void*>(gemm_prefill_kernel<false, false>)
+                     : variant == 1 ? reinterpret_cast<const void*>(gemm_prefill_kernel<true, false>)
+                                    : reinterpret_cast<const void*>(gemm_prefill_kernel<true, true>);
+  const hipError_t ea = ensure_dynamic_lds(lds_opt_in[variant], kern, (int)kPrefillLds);
   if (ea != hipSuccess) return ea;
   // Down GEMM with a long K (= I): an M-tile's column blocks share one XCD,
   // whose L2 then takes the tile's activation rows (256 x I fp16) once
@@ -752,14 +801,17 @@ hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a
     blocks = (blocks + span - 1) / span * span;   // padding blocks find no tile and exit
   }
   const dim3 grid(blocks);
-  if (gate_up && (kt.start || kt.stop))
-    hipExtLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPrefillThreads),
-                          (uint32_t)kPrefillLds, s, kt.start, kt.stop, 0, a);
-  else if (gate_up)
-    hipLaunchKernelGGL(gemm_prefill_kernel<true>, grid, dim3(kPrefillThreads), kPrefillLds, s, a);
-  else
-    hipLaunchKernelGGL(gemm_prefill_kernel<false>, grid, dim3(kPrefillThreads), kPrefillLds, s, a);
-  return hipGetLastError();
+  auto run = [&](auto kern) {
+    if (gate_up && (kt.start || kt.stop))
+      hipExtLaunchKernelGGL(kern, grid, dim3(kPrefillThreads), (uint32_t)kPrefillLds, s, kt.start,
+                            kt.stop, 0, a);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(kPrefillThreads), kPrefillLds, s, a);
+    return hipGetLastError();
+  };
+  if (variant == 0) return run(gemm_prefill_kernel<false, false>);
+  if (variant == 1) return run(gemm_prefill_kernel<true, false>);
+  return run(gemm_prefill_kernel<true, true>);
 }
 
 }  // namespace moe

@@ -586,47 +586,66 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-constexpr double kDecodeRows8Max = 4.0;   // mean rows per expert up to which tiles are 8 rows
+constexpr double kDecodeRows8Max = 4.0;    // mean routes per expert up to which tiles are 8 rows
 constexpr double kDecodeRows16Max = 12.0;  // ... 16 rows
-constexpr double kDecodeRows32Max = 24.0;  // ... 32 rows (unless the launch splits K)
-// ... 64 rows: layers whose large-batch gate/up grid fills the 256 CUs six or
-// more times (many experts), and the others
-constexpr double kDecodeRows64MaxWide = 64.0, kDecodeRows64Max = 40.0;
+// Layers whose decode launches have at least kManyDecodeWaves waves (one per
+// 64 output columns of one tile per touched expert, the narrower GEMM): 64-row
+// tiles up to kDecodeRows64Max, then the mixed plan up to the bound below,
+// then the large-batch kernel for both GEMMs.  Layers with fewer (few
+// experts, as the Mixtral shape): 32-row tiles up to kFewWavesRows32Max,
+// then the large-batch kernel.
+constexpr long kManyDecodeWaves = 2048;
+constexpr double kDecodeRows64Max = 40.0;
+constexpr double kFewWavesRows32Max = 20.0;
+constexpr double kMixedRowsMaxShortI = 128.0;   // expert intermediate size I <= 512
+constexpr double kMixedRowsMax = 56.0;          // wider I
 
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
-  const double rows_per_expert = (double)T * L.k / L.E;
-  // Decode tiles stream each expert's weights once per tile with exact
-  // integer operands; the large-batch kernel (256-row tiles, fp16 MFMA) runs
-  // one 512-thread block per CU and is latency-bound over K when its tiles
-  // are far from full.  The boundaries below come from sweeps on one MI355X:
-  //   * 8-row tiles while few experts overflow them (the LDS staging then
-  //     fits any K up to 4096 in one chunk); 16-row tiles above;
-  //   * 32-row tiles (two waves per SIMD) between 12 and 24 mean rows, where
-  //     they stream most experts' weights once instead of twice: Mixtral
-  //     T = 64 277 -> 259 us, Qwen3-80B T = 1024 397 -> 371 us, Zipf-biased
-  //     Qwen3-30B T = 256 206 -> 183 us; not with the few tiles of a split-K
-  //     launch (the tiny layer: 12% slower);
-  //   * 64-row tiles above 24 mean rows: Qwen3-80B T = 2048 596 -> 520 us
-  //     (against 16-row tiles) and T = 3072 772 -> 699 us (against the large-
-  //     batch kernel), OLMoE T = 256 131 -> 117 us, Zipf-biased Qwen3-30B
-  //     T = 512 232 -> 208 us; the large-batch kernel stays ahead from
-  //     64 rows (OLMoE T = 512 160 vs 186 us, Mixtral T = 256 508 vs 611 us)
-  //     and at 80 on the many-expert layer (Qwen3-80B T = 4096 910 vs 952 us).
-  const double rounds = (double)L.E * (2.0 * L.I / 256.0) / 256.0;
-  const double decode_max = rounds >= 6.0 ? kDecodeRows64MaxWide : kDecodeRows64Max;
-  const bool decode = rows_per_expert <= decode_max;
-  p.kind = decode ? kGemmDecode : kGemmPrefill;
-  int bm = 256;
-  if (decode) {
-    const bool split = decode_split_k(L, T, 2 * L.I);   // the gate/up launch would split K
-    bm = rows_per_expert <= kDecodeRows8Max    ? 8
-         : rows_per_expert <= kDecodeRows16Max ? 16
-         : rows_per_expert <= kDecodeRows32Max ? (split ? 16 : 32)
-                                               : 64;
+  const double rows = (double)T * L.k / L.E;
+  // The boundaries come from per-GEMM sweeps on one MI355X (kernel times in
+  // us, gate/up + down, at the mean routes per expert given):
+  //   * 64-row decode tiles (row-skipping, so an expert of up to 64 routes
+  //     streams its weights once) beat 32-row ones from 12 routes on layers
+  //     with many waves: Qwen3-80B shape at 20 routes 274 vs 284, OLMoE at 24
+  //     76 vs 93, Zipf-biased Qwen3-30B at 16 and 24 117 vs 146 and 139 vs 184;
+  //   * from 40 routes the large-batch gate/up GEMM wins there (Qwen3-80B
+  //     at 50: 248 vs 289; OLMoE at 48: 53 vs 64) while the decode down GEMM
+  //     keeps winning on short I (Qwen3-80B I = 512: 188 vs 266 at 50, 224
+  //     vs 302 at 60, 303 vs 369 at 80): gate/up + down 436 vs 476 at 50,
+  //     480 vs 570 at 60, 586 vs 652 at 80; on OLMoE (I = 1024) only up to
+  //     about 56 (93 vs 97 at 48, 114 vs 110 at 64);
+  //   * with few waves (Mixtral shape: 8 experts, 64 down-GEMM column strips
+  //     each) 64-row decode tiles leave the GPU mostly idle: 32-row tiles up
+  //     to 20 routes (234 vs 247 large-batch at 16), the large-batch kernel
+  //     above (249 vs 270 at 24, 283 vs 431 at 40).
+  const long tiles = est_decode_tiles(L, T);
+  const bool many_waves = tiles * (std::min(2 * L.I, L.H) / 64) >= kManyDecodeWaves;
+  int bm13 = 256, bm2 = 256;
+  bool dec13 = false, dec2 = false;
+  if (rows <= kDecodeRows8Max) {
+    bm13 = bm2 = 8;
+    dec13 = dec2 = true;
+  } else if (rows <= kDecodeRows16Max) {
+    bm13 = bm2 = 16;
+    dec13 = dec2 = true;
+  } else if (many_waves) {
+    if (rows <= kDecodeRows64Max) {
+      bm13 = bm2 = 64;
+      dec13 = dec2 = true;
+    } else if (rows <= (L.I <= 512 ? kMixedRowsMaxShortI : kMixedRowsMax)) {
+      bm2 = 64;
+      dec2 = true;
+    }
+  } else if (rows <= kFewWavesRows32Max) {
+    // not with the few tiles of a split-K launch (the tiny layer: 12% slower)
+    bm13 = bm2 = decode_split_k(L, T, 2 * L.I) ? 16 : 32;
+    dec13 = dec2 = true;
   }
-  p.bm13 = bm;
-  p.bm2 = p.bm13;
+  p.bm13 = bm13;
+  p.bm2 = bm2;
+  p.kind = dec13 ? kGemmDecode : kGemmPrefill;
+  p.kind2 = dec2 ? kGemmDecode : kGemmPrefill;
   return p;
 }
 
@@ -666,7 +685,7 @@ hipError_t launch_gemm2(const Layer& L, const GemmPlan& gp, int T, const uint16_
   a.N = L.H;
   a.topk_w = topk_w;
   a.rows = rows;
-  if (gp.kind != kGemmDecode) return hipErrorInvalidValue;
+  if (gp.kind2 != kGemmDecode) return hipErrorInvalidValue;
   const bool ks = gp.bm2 < 64 && decode_split_k(L, T, a.N);
   // Very few column blocks even with split K (a wide-K, narrow-N down GEMM
   // over one or two tiles, e.g. the Mixtral shape at one token): two strips

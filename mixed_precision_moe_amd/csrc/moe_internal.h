@@ -70,10 +70,15 @@ static_assert(sizeof(TileEntry) == 32, "tile entry is one 32-byte scalar load");
 // and the layer: decode (few routes per expert, weight streaming, exact
 // integer MFMA operands) or prefill (many routes per expert, fp16 MFMA).
 enum GemmKind { kGemmDecode = 1, kGemmPrefill = 2 };
+// Each grouped GEMM takes its own kernel family and M-tiling.  The one mixed
+// plan is a large-batch gate/up GEMM feeding a decode down GEMM: its epilogue
+// then writes bf16 activations and their 32-column row sums, as the decode
+// gate/up epilogue does.
 struct GemmPlan {
   int bm13;   // rows per M-tile, gate/up GEMM
   int bm2;    // rows per M-tile, down GEMM
-  int kind;   // GemmKind
+  int kind;   // GemmKind of the gate/up GEMM
+  int kind2;  // GemmKind of the down GEMM
 };
 
 // Byte offsets of the workspace regions for T tokens.
@@ -206,7 +211,8 @@ size_t prefill_lds_bytes();
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* x16, size_t n, hipStream_t s);
 hipError_t launch_prefill(bool gate_up, const Layer& L, int T, const uint16_t* a16, const int32_t* sorted,
                           const TileEntry* tiles, const int32_t* ntiles, int max_tiles,
-                          uint16_t* act16, const float* topk_w, float* rows, hipStream_t s, KernelTimer kt = KernelTimer{nullptr, nullptr});
+                          uint16_t* act16, float* r2, const float* topk_w, float* rows,
+                          hipStream_t s, KernelTimer kt = KernelTimer{nullptr, nullptr});
 // y[t] (=|+=) sum over the token's routes in ascending expert order (rows
 // [T k, H] by route id); with a slot map, routes whose expert maps to the
 // sentinel are skipped.

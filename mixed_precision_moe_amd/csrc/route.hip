@@ -314,19 +314,16 @@ __device__ __forceinline__ TileSource tile_source(const DevHandle* table, WaveMa
 constexpr int kSortTilesMinBm = 64;
 constexpr int kMaxTileRows = 256;
 
-__device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness hotness,
-                                                  const int* off, int E,
-                                                  TileEntry* tiles13, int32_t* ntiles13,
-                                                  TileEntry* tiles2, int32_t* ntiles2, int bm,
-                                                  int* scan, int* hist) {
+// The M-tiles of bm rows of every expert, written to tiles13 (with the
+// gate/up weights) and/or tiles2 (with the down weights), whichever is
+// non-null: both when the two GEMMs share one M-tiling.
+__device__ __forceinline__ void place_tiles(const TileSource& src, const int* off, int E,
+                                            TileEntry* tiles13, int32_t* ntiles13,
+                                            TileEntry* tiles2, int32_t* ntiles2, int bm,
+                                            int* scan, int* hist) {
   const int tid = threadIdx.x;
-  // DynaExq hotness from the router trace: decayed count of routes per expert
-  if (hotness.hot && tid < E)
-    hotness.hot[tid] = hotness.decay * hotness.hot[tid] + (float)(off[tid + 1] - off[tid]);
   const DevHandle& h = src.h;
   const bool active = src.active;
-  // Both GEMMs use the same M-tiling: one pass places every tile and writes
-  // it to both tables, with the gate/up and the down weights.
   const int ce = tid < E && active ? off[tid + 1] - off[tid] : 0;
   auto put = [&](int at, int i, int rows) {
     TileEntry te2;
@@ -335,10 +332,14 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
     te2.rows = rows;
     te2.tier = h.tier;
     te2.pad = 0;
-    te2.w = h.w13;
-    tiles13[at] = te2;
-    te2.w = h.w2;
-    tiles2[at] = te2;
+    if (tiles13) {
+      te2.w = h.w13;
+      tiles13[at] = te2;
+    }
+    if (tiles2) {
+      te2.w = h.w2;
+      tiles2[at] = te2;
+    }
   };
   int count = 0, many = 0;
   if (bm < kSortTilesMinBm || bm > kMaxTileRows) {   // block-uniform
@@ -372,8 +373,32 @@ __device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness
   // ntiles[1]: some expert spans three or more decode tiles (the decode
   // GEMMs then keep an expert's sub-tiles on one XCD)
   if (tid == 0) {
-    ntiles13[0] = ntiles2[0] = count;
-    ntiles13[1] = ntiles2[1] = many;
+    if (ntiles13) {
+      ntiles13[0] = count;
+      ntiles13[1] = many;
+    }
+    if (ntiles2) {
+      ntiles2[0] = count;
+      ntiles2[1] = many;
+    }
+  }
+}
+
+__device__ __forceinline__ void write_tile_tables(const TileSource& src, Hotness hotness,
+                                                  const int* off, int E,
+                                                  TileEntry* tiles13, int32_t* ntiles13, int bm13,
+                                                  TileEntry* tiles2, int32_t* ntiles2, int bm2,
+                                                  int* scan, int* hist) {
+  const int tid = threadIdx.x;
+  // DynaExq hotness from the router trace: decayed count of routes per expert
+  if (hotness.hot && tid < E)
+    hotness.hot[tid] = hotness.decay * hotness.hot[tid] + (float)(off[tid + 1] - off[tid]);
+  if (bm13 == bm2) {   // one pass places every tile in both tables
+    place_tiles(src, off, E, tiles13, ntiles13, tiles2, ntiles2, bm13, scan, hist);
+  } else {
+    place_tiles(src, off, E, tiles13, ntiles13, nullptr, nullptr, bm13, scan, hist);
+    __syncthreads();   // scan and hist serve the second table
+    place_tiles(src, off, E, nullptr, nullptr, tiles2, ntiles2, bm2, scan, hist);
   }
 }
 
@@ -389,7 +414,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     const DevHandle* __restrict__ table, WaveMap wmap, Hotness hotness, const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
     int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
-    int32_t* __restrict__ ntiles2) {
+    int32_t* __restrict__ ntiles2, int bm2) {
   extern __shared__ int lds[];
   int* cnt = lds;                 // [16][E]
   int* off = cnt + 16 * E;        // [E+1] exclusive scan of totals
@@ -443,7 +468,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
   __syncthreads();
 
-  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, tiles2, ntiles2, bm13, scan, hist);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan, hist);
 }
 
 // Rank pass of the multi-block grouping (large T).  Block c owns the 256
@@ -529,7 +554,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
     const int32_t* __restrict__ chunk_tot, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted, int32_t* __restrict__ pos, TileEntry* __restrict__ tiles13,
     int32_t* __restrict__ ntiles13, int bm13, TileEntry* __restrict__ tiles2,
-    int32_t* __restrict__ ntiles2) {
+    int32_t* __restrict__ ntiles2, int bm2) {
   __shared__ int base[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int scan[16];
@@ -556,7 +581,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(
   }
   if (c != 0) return;
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
-  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, tiles2, ntiles2, bm13, scan, hist);
+  write_tile_tables(src, hotness, off, E, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2, scan, hist);
 }
 
 }  // namespace
@@ -626,7 +651,6 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
                           TileEntry* tiles13, int32_t* ntiles13, int bm13, TileEntry* tiles2,
                           int32_t* ntiles2, int bm2, int32_t* rank, int32_t* chunk_counts,
                           int32_t* chunk_tot, hipStream_t s) {
-  if (bm13 != bm2) return hipErrorInvalidValue;   // the two GEMMs share one M-tiling
   if (T > kPermSmallT) {
     const int nchunks = (T + kPermChunk - 1) / kPermChunk;
     hipLaunchKernelGGL(permute_rank_kernel, dim3(nchunks), dim3(256), 0, s, ids, T, k, E, rank,
@@ -639,7 +663,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(1024), 0, s, table, wave, hotness, ids, T, k, E,
                        rank, chunk_counts, chunk_tot, offsets, sorted, pos, tiles13, ntiles13, bm13,
-                       tiles2, ntiles2);
+                       tiles2, ntiles2, bm2);
     return hipGetLastError();
   }
   const size_t lds = sizeof(int) * (17 * (size_t)E + 1025 + kMaxTileRows + (size_t)T * k);
@@ -651,7 +675,7 @@ hipError_t launch_permute(const DevHandle* table, WaveMap wave, Hotness hotness,
       (int)(sizeof(int) * (17 * kMaxExperts + 1025 + kMaxTileRows + kPermSmallT * kMaxTopK)));
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, table, wave, hotness, ids, T, k, E, offsets, sorted,
-                     pos, tiles13, ntiles13, bm13, tiles2, ntiles2);
+                     pos, tiles13, ntiles13, bm13, tiles2, ntiles2, bm2);
   return hipGetLastError();
 }
 

@@ -42,9 +42,10 @@ def _run(st: Setup, layer=None, subset=None, keep=True, runs=2):
     if layer is None:
         layer = st.gpu_layer()
     x, wr, b = st.dev_inputs()
-    path, bm = layer.plan(st.T)
+    (path13, bm13), (path2, bm2) = layer.plan_gemms(st.T)
+    path = max(path13, path2)         # the tolerance of the looser GEMM
     log(f"forward cfg{st.cfg.cid} T={st.T} tiers={np.bincount(st.tiers, minlength=3).tolist()} "
-        f"path={path} tile_rows={bm}")
+        f"gate/up path={path13} tile_rows={bm13}, down path={path2} tile_rows={bm2}")
     y32 = layer.forward(x, wr, b, out_dtype=torch.float32)
     y16 = layer.forward(x, wr, b, out_dtype=torch.bfloat16)
     y32b = layer.forward(x, wr, b, out_dtype=torch.float32) if runs > 1 else y32
@@ -56,8 +57,8 @@ def _run(st: Setup, layer=None, subset=None, keep=True, runs=2):
     ol = st.oracle_layer()
     r = oracle.route(st.x, st.wr, st.bias, st.k)
     if isinstance(subset, str):
-        subset = tile_boundary_tokens(r, st.E, bm)
-        log(f"  comparing {len(subset)} tokens: the first and last row of every M-tile")
+        subset = np.union1d(tile_boundary_tokens(r, st.E, bm13), tile_boundary_tokens(r, st.E, bm2))
+        log(f"  comparing {len(subset)} tokens: the first and last row of every M-tile of both GEMMs")
     get = ol.expert if keep else ol._build
     y_ref = oracle.layer_forward(st.x, r, get, subset)
     got = y32n if subset is None else y32n[subset]
@@ -77,17 +78,17 @@ def test_layer_small_configs_full(cid):
 @pytest.mark.parametrize("T", [32, 64, 128, 256, 512])
 def test_layer_olmoe_full(T):
     """The OLMoE-shaped layer (H 2048, E 64, top-8, I 1024): decode with 8-row
-    tiles (T 32), with 16- and 32-row tiles staged in two K-chunks (T 64, 128:
-    8 and 16 rows per expert on average), with 64-row tiles (T 256: 32 rows
-    per expert, ragged), and the large-batch path (T 512)."""
+    tiles (T 32), with 16-row tiles staged in two K-chunks (T 64: 8 rows per
+    expert on average), with 64-row tiles (T 128, 256: 16 and 32 rows per
+    expert, ragged), and the large-batch path (T 512)."""
     _run(Setup(6, T=T))
 
 
 @pytest.mark.parametrize("T", [40, 80, 200])
 def test_layer_mixed_tiers_skewed_decode(T):
     """Qwen3-30B shape with bf16, int8 and int4 experts and the Zipf bias at
-    2.5, 5 and 12.5 rows per expert on average: 8- and 16-row decode tiles,
-    hot experts spanning several tiles (their tiles grouped by XCD)."""
+    2.5, 5 and 12.5 rows per expert on average: 8-, 16- and 64-row decode
+    tiles, hot experts spanning several tiles (their tiles grouped by XCD)."""
     _run(Setup(3, T=T), keep=False)
 
 
@@ -99,15 +100,22 @@ def test_layer_qwen80b_sweep_full(T):
 @pytest.mark.parametrize("T", [1024, 2048])
 def test_layer_qwen80b_mid_full(T):
     """512 experts at 20 and 40 rows per expert on average: the decode kernels
-    with 32-row tiles (experts spanning up to four tiles) and with 64-row
-    tiles; every output compared."""
+    with 64-row tiles (experts spanning up to three tiles, row blocks past an
+    expert's routes skipped); every output compared."""
+    assert Setup(4, T=8).gpu_layer(experts=[0]).plan_gemms(T) == ((1, 64), (1, 64))
     _run(Setup(4, T=T), keep=False)
 
 
-def test_layer_qwen80b_4096_tiles():
-    """80 rows per expert: the large-batch kernels with row-aware partial
-    tiles; the first and last row of every M-tile compared."""
-    _run(Setup(4, T=4096), subset="tiles", keep=False)
+@pytest.mark.parametrize("T", [2560, 4096])
+def test_layer_qwen80b_mixed_plan_tiles(T):
+    """50 and 80 rows per expert: the large-batch gate/up GEMM (row-aware
+    partial tiles) writes bf16 activations and their 32-column row sums for
+    the decode down GEMM with 64-row tiles; the first and last row of every
+    M-tile of both GEMMs compared."""
+    st = Setup(4, T=T)
+    layer = st.gpu_layer()
+    assert layer.plan_gemms(T) == ((2, 256), (1, 64))
+    _run(st, layer=layer, subset="tiles", keep=False)
 
 
 def test_layer_mixtral_prefill_tiles():
@@ -137,18 +145,18 @@ def test_layer_decode_ragged_k_chunks():
 def test_layer_large_batch_ragged_k(T):
     """A layer whose K-chunk counts are odd (hidden 4352, inter 4224: 34 and
     33 steps of two 64-wide chunks), all routes on experts 0 (int4) and 3
-    (int8) at T rows each.  Above 40 mean rows per expert (T > 80) the
+    (int8) at T rows each.  With four experts the decode launches would have
+    few waves, so from 20 mean rows per expert (every T here) the
     large-batch kernels run: int4 tiles of at most 128 rows split K between
     the block's two wave rows (the down GEMM with a last single step), larger
-    ones split rows; at T = 65 the decode kernels with 64-row tiles (a full
-    tile and a one-row tile per expert)."""
+    ones split rows."""
     c = dataclasses.replace(inputs.get_config(1), hidden=4352, inter=4224, n_experts=4,
                             top_k=2, max_tokens=200)
     b = np.zeros(4, np.float32)
     b[[0, 3]] = 100.0
     st = Setup(1, T=T, cfg=c, bias=b, tiers=np.array([2, 0, 2, 1]))
     layer = st.gpu_layer(experts=[0, 3])
-    assert layer.plan(T) == ((2, 256) if T > 80 else (1, 64))
+    assert layer.plan_gemms(T) == ((2, 256), (2, 256))
     _run(st, layer=layer, keep=False, runs=1)
 
 
@@ -247,11 +255,26 @@ def test_handle_swap_promotes_expert():
 
 
 def test_plan_query():
-    """moe_layer_plan names the path each workload takes: the decode batches
-    stream weights (path 1), the Mixtral prefill runs on the large-batch
-    kernels (path 2) with 256-row tiles."""
+    """moe_layer_plan names the path and M-tiling of each GEMM: the decode
+    batches stream weights (path 1); the Mixtral prefill, and the Mixtral
+    shape already from 24 routes per expert (few experts, so few decode
+    waves), run on the large-batch kernels (path 2) with 256-row tiles; the
+    many-expert Qwen3-80B shape takes 64-row decode tiles up to 40 routes per
+    expert and then pairs the large-batch gate/up GEMM with the decode down
+    GEMM (its I = 512 is short)."""
     assert Setup(2).gpu_layer(experts=[0]).plan(32)[0] == 1
-    assert Setup(5, T=1).gpu_layer(experts=[0]).plan(8192) == (2, 256)
+    mixtral = Setup(5, T=1).gpu_layer(experts=[0])
+    assert mixtral.plan(8192) == (2, 256)
+    assert mixtral.plan_gemms(64) == ((1, 32), (1, 32))
+    assert mixtral.plan_gemms(96) == ((2, 256), (2, 256))
+    q80 = Setup(4, T=1).gpu_layer(experts=[0])
+    assert q80.plan_gemms(1) == ((1, 8), (1, 8))
+    assert q80.plan_gemms(2048) == ((1, 64), (1, 64))
+    assert q80.plan_gemms(2049) == ((2, 256), (1, 64))
+    assert q80.plan_gemms(4096) == ((2, 256), (1, 64))
+    olmoe = Setup(6, T=1).gpu_layer(experts=[0])
+    assert olmoe.plan_gemms(384) == ((2, 256), (1, 64))
+    assert olmoe.plan_gemms(512) == ((2, 256), (2, 256))
 
 
 def test_large_batch_32bit_offset_limit():

@@ -91,9 +91,9 @@ def _big_bias(st):
     st.bias = b
 
 
-def _small_cfg(E, H, k):
+def _small_cfg(E, H, k, max_tokens=64):
     return dataclasses.replace(inputs.get_config(1), hidden=H, n_experts=E, top_k=k,
-                               max_tokens=64)
+                               max_tokens=max_tokens)
 
 
 @pytest.mark.parametrize("cid,T,mutate,shape", [
@@ -121,6 +121,14 @@ def test_small_router_matches_canonical(cid, T, mutate, shape):
     ref = oracle.route(st.x, st.wr, st.bias, st.k)
     assert np.array_equal(fast["ids"], ref["ids"])
     assert np.max(np.abs(fast["weights"] - ref["weights"])) <= 1e-6
+
+
+@pytest.mark.parametrize("T", [64, 3, 200])
+def test_route_1024_experts_top16(T):
+    """The largest expert count and top-k the library takes (1024 experts,
+    top-16, 512 KiB of router weights): the top-k kernel holds 16 entries per
+    lane.  Routing bit-exact against the oracle."""
+    _check_route(Setup(1, T=T, cfg=_small_cfg(1024, 256, 16, max_tokens=256)))
 
 
 def _mfma_layer(st):
