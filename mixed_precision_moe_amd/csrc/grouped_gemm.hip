@@ -209,6 +209,13 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
   // 16-row MFMA blocks holding a real row of the tile (the others are skipped:
   // their rows are never stored)
   const int nrb = uniform((rows + 15) >> 4);
+  // The tile's A rows: lane m < rows holds row m's first element in a_src
+  // (every wave holds the same), for the staging DMAs below.
+  int64_t row_elem = 0;
+  if (lane < rows) {
+    const int pos = te.row_start + lane;
+    row_elem = GATE_UP ? (int64_t)(a.sorted[pos] / a.top_k) * K : (int64_t)pos * K;
+  }
   int c0 = 0;
   auto consume = [&](int g, int d) {
     const int gl = g - c0;
@@ -271,18 +278,31 @@ __device__ __forceinline__ void decode_mainloop(const GemmArgs& a, const TileEnt
       if (w0 + d < c1) issue(w0 + d, d);
     if (c0 > 0) __syncthreads();   // every wave is done with the previous chunk's A
 
-    // stage this chunk's A columns and group sums (block-wide)
+    // stage this chunk's A columns and group sums (block-wide).  A rows go
+    // from memory straight into LDS (buffer_load ... lds): one instruction
+    // moves a 1 KB segment of one row (16 bytes per lane, lanes past a ragged
+    // segment's end masked off), and a wave issues all of its segments back
+    // to back, so the staging costs about one memory round trip.  (A loop of
+    // 16-byte loads through registers waited for each load before its LDS
+    // store: 16 round trips for a 64-row tile's 512 columns.)
     {
       const int ce = cs + GC < G ? cs + GC : G;
-      const int kc = (ce - cs) * kGroup;
-      const int chunks = rows * (kc / 8);
-      for (int c = threadIdx.x; c < chunks; c += 64 * WAVES) {
-        const int m = c / (kc / 8), col = 8 * (c - m * (kc / 8));
-        const int pos = te.row_start + m;
-        const size_t kcol = (size_t)cs * kGroup + col;
-        const uint16_t* src = GATE_UP ? a.a_src + (size_t)(a.sorted[pos] / a.top_k) * K + kcol
-                                      : a.a_src + (size_t)pos * K + kcol;
-        *reinterpret_cast<uint4*>(lds_a + m * lda + col) = *reinterpret_cast<const uint4*>(src);
+      const int kcb = (ce - cs) * kGroup * 2;             // bytes of one row in this chunk
+      const int segs = (kcb + 1023) >> 10;
+      typedef __attribute__((address_space(3))) uint8_t lds_b;
+      lds_b* lbase = (lds_b*)lds_a;
+      for (int t = uniform(threadIdx.x >> 6); t < rows * segs; t += WAVES) {   // wave-uniform
+        const int m = t / segs, j = t - m * segs;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)row_elem, m);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)row_elem >> 32), m);
+        const uint16_t* rowp = a.a_src + (int64_t)(((uint64_t)hi << 32) | lo) +
+                               (size_t)cs * kGroup + (size_t)j * 512;
+        const int left = kcb - j * 1024;                   // >= 256
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(rowp, (uint32_t)(left < 1024 ? left : 1024));
+        if (16 * lane < left)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rr, (__attribute__((address_space(3))) void*)(lbase + 2 * (m * lda + j * 512)), 16,
+              16 * lane, 0, 0, 0);
       }
       if constexpr (TIER != MOE_TIER_BF16) {
         for (int i = threadIdx.x; i < (ce - cs) * RS; i += 64 * WAVES) {
