@@ -610,35 +610,38 @@ constexpr double kDecodeRows8Max = 4.0;    // mean routes per expert up to which
 constexpr double kDecodeRows16Max = 12.0;  // ... 16 rows
 // Layers whose decode launches have at least kManyDecodeWaves waves (one per
 // 64 output columns of one tile per touched expert, the narrower GEMM): 64-row
-// tiles up to kDecodeRows64Max, then the mixed plan up to the bound below,
-// then the large-batch kernel for both GEMMs.  Layers with fewer (few
-// experts, as the Mixtral shape): 32-row tiles up to kFewWavesRows32Max,
-// then the large-batch kernel.
+// tiles up to kDecodeRows64Max, then (I <= 512) the mixed plan up to
+// kMixedRowsMax, then the large-batch kernel for both GEMMs.  Layers with
+// fewer (few experts, as the Mixtral shape): 32-row tiles up to
+// kFewWavesRows32Max, then the large-batch kernel.
 constexpr long kManyDecodeWaves = 2048;
-constexpr double kDecodeRows64Max = 40.0;
-constexpr double kFewWavesRows32Max = 20.0;
-constexpr double kMixedRowsMaxShortI = 128.0;   // expert intermediate size I <= 512
-constexpr double kMixedRowsMax = 56.0;          // wider I
+constexpr double kDecodeRows64Max = 60.0;
+constexpr double kMixedRowsMax = 128.0;
+constexpr double kFewWavesRows32Max = 28.0;
 
 GemmPlan plan_gemm(const Layer& L, int T) {
   GemmPlan p;
   const double rows = (double)T * L.k / L.E;
-  // The boundaries come from per-GEMM sweeps on one MI355X (kernel times in
-  // us, gate/up + down, at the mean routes per expert given):
+  // The boundaries come from per-GEMM sweeps on one MI355X (gate/up + down
+  // kernel times in us at the mean routes per expert given):
+  //   * 8- and 16-row tiles for few routes: the Qwen3-30B shape at 2 routes
+  //     53.6 (8 rows) against 70.2 (64 rows), the Qwen3-80B shape at 5 and
+  //     10 routes 171 and 189 (16 rows) against 206 and 218 (64 rows);
   //   * 64-row decode tiles (row-skipping, so an expert of up to 64 routes
-  //     streams its weights once) beat 32-row ones from 12 routes on layers
-  //     with many waves: Qwen3-80B shape at 20 routes 274 vs 284, OLMoE at 24
-  //     76 vs 93, Zipf-biased Qwen3-30B at 16 and 24 117 vs 146 and 139 vs 184;
-  //   * from 40 routes the large-batch gate/up GEMM wins there (Qwen3-80B
-  //     at 50: 248 vs 289; OLMoE at 48: 53 vs 64) while the decode down GEMM
-  //     keeps winning on short I (Qwen3-80B I = 512: 188 vs 266 at 50, 224
-  //     vs 302 at 60, 303 vs 369 at 80): gate/up + down 436 vs 476 at 50,
-  //     480 vs 570 at 60, 586 vs 652 at 80; on OLMoE (I = 1024) only up to
-  //     about 56 (93 vs 97 at 48, 114 vs 110 at 64);
+  //     streams its weights once) from 12 routes on layers with many waves:
+  //     Qwen3-80B at 15, 40, 50 routes 222, 322, 376 against 235 (16 rows),
+  //     490 and 514 (large batch); OLMoE at 24 and 48 62 and 86 against 71
+  //     (16 rows) and 98 (large batch);
+  //   * past 60 routes the large-batch gate/up GEMM wins there while the
+  //     decode down GEMM keeps winning on short I: Qwen3-80B (I = 512) at 70
+  //     and 80 routes 514 and 546 (mixed) against 568 and 622 (64 rows) and
+  //     609 and 647 (large batch); OLMoE (I = 1024) at 64 routes 110 either
+  //     way, 122 with 64-row tiles;
   //   * with few waves (Mixtral shape: 8 experts, 64 down-GEMM column strips
-  //     each) 64-row decode tiles leave the GPU mostly idle: 32-row tiles up
-  //     to 20 routes (234 vs 247 large-batch at 16), the large-batch kernel
-  //     above (249 vs 270 at 24, 283 vs 431 at 40).
+  //     each) 64-row tiles leave the GPU mostly idle: 32-row tiles up to 28
+  //     routes (24 and 28 routes: 196 and 198 against 253 and 249 large
+  //     batch), the large-batch kernel above (32 and 40 routes: 269 and 285
+  //     against 298 and 383).
   const long tiles = est_decode_tiles(L, T);
   const bool many_waves = tiles * (std::min(2 * L.I, L.H) / 64) >= kManyDecodeWaves;
   int bm13 = 256, bm2 = 256;
@@ -653,7 +656,7 @@ GemmPlan plan_gemm(const Layer& L, int T) {
     if (rows <= kDecodeRows64Max) {
       bm13 = bm2 = 64;
       dec13 = dec2 = true;
-    } else if (rows <= (L.I <= 512 ? kMixedRowsMaxShortI : kMixedRowsMax)) {
+    } else if (L.I <= 512 && rows <= kMixedRowsMax) {
       bm2 = 64;
       dec2 = true;
     }

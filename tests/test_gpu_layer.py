@@ -100,18 +100,18 @@ def test_layer_qwen80b_sweep_full(T):
 @pytest.mark.parametrize("T", [1024, 2048])
 def test_layer_qwen80b_mid_full(T):
     """512 experts at 20 and 40 rows per expert on average: the decode kernels
-    with 64-row tiles (experts spanning up to three tiles, row blocks past an
-    expert's routes skipped); every output compared."""
+    with 64-row tiles (row blocks past an expert's routes skipped, the rows
+    staged into LDS by DMA); every output compared."""
     assert Setup(4, T=8).gpu_layer(experts=[0]).plan_gemms(T) == ((1, 64), (1, 64))
     _run(Setup(4, T=T), keep=False)
 
 
-@pytest.mark.parametrize("T", [2560, 4096])
+@pytest.mark.parametrize("T", [3584, 4096])
 def test_layer_qwen80b_mixed_plan_tiles(T):
-    """50 and 80 rows per expert: the large-batch gate/up GEMM (row-aware
+    """70 and 80 rows per expert: the large-batch gate/up GEMM (row-aware
     partial tiles) writes bf16 activations and their 32-column row sums for
-    the decode down GEMM with 64-row tiles; the first and last row of every
-    M-tile of both GEMMs compared."""
+    the decode down GEMM with 64-row tiles (experts spanning two); the first
+    and last row of every M-tile of both GEMMs compared."""
     st = Setup(4, T=T)
     layer = st.gpu_layer()
     assert layer.plan_gemms(T) == ((2, 256), (1, 64))
@@ -146,7 +146,7 @@ def test_layer_large_batch_ragged_k(T):
     """A layer whose K-chunk counts are odd (hidden 4352, inter 4224: 34 and
     33 steps of two 64-wide chunks), all routes on experts 0 (int4) and 3
     (int8) at T rows each.  With four experts the decode launches would have
-    few waves, so from 20 mean rows per expert (every T here) the
+    few waves, so past 28 mean rows per expert (every T here) the
     large-batch kernels run: int4 tiles of at most 128 rows split K between
     the block's two wave rows (the down GEMM with a last single step), larger
     ones split rows."""
@@ -257,24 +257,27 @@ def test_handle_swap_promotes_expert():
 def test_plan_query():
     """moe_layer_plan names the path and M-tiling of each GEMM: the decode
     batches stream weights (path 1); the Mixtral prefill, and the Mixtral
-    shape already from 24 routes per expert (few experts, so few decode
+    shape already past 28 routes per expert (few experts, so few decode
     waves), run on the large-batch kernels (path 2) with 256-row tiles; the
-    many-expert Qwen3-80B shape takes 64-row decode tiles up to 40 routes per
+    many-expert Qwen3-80B shape takes 64-row decode tiles up to 60 routes per
     expert and then pairs the large-batch gate/up GEMM with the decode down
-    GEMM (its I = 512 is short)."""
-    assert Setup(2).gpu_layer(experts=[0]).plan(32)[0] == 1
+    GEMM (its I = 512 is short); the OLMoE shape (I = 1024) goes from 64-row
+    tiles straight to the large-batch kernels."""
+    assert Setup(2).gpu_layer(experts=[0]).plan(32) == (1, 8)
     mixtral = Setup(5, T=1).gpu_layer(experts=[0])
     assert mixtral.plan(8192) == (2, 256)
     assert mixtral.plan_gemms(64) == ((1, 32), (1, 32))
-    assert mixtral.plan_gemms(96) == ((2, 256), (2, 256))
+    assert mixtral.plan_gemms(112) == ((1, 32), (1, 32))
+    assert mixtral.plan_gemms(113) == ((2, 256), (2, 256))
     q80 = Setup(4, T=1).gpu_layer(experts=[0])
     assert q80.plan_gemms(1) == ((1, 8), (1, 8))
-    assert q80.plan_gemms(2048) == ((1, 64), (1, 64))
-    assert q80.plan_gemms(2049) == ((2, 256), (1, 64))
+    assert q80.plan_gemms(512) == ((1, 16), (1, 16))
+    assert q80.plan_gemms(3072) == ((1, 64), (1, 64))
+    assert q80.plan_gemms(3073) == ((2, 256), (1, 64))
     assert q80.plan_gemms(4096) == ((2, 256), (1, 64))
     olmoe = Setup(6, T=1).gpu_layer(experts=[0])
-    assert olmoe.plan_gemms(384) == ((2, 256), (1, 64))
-    assert olmoe.plan_gemms(512) == ((2, 256), (2, 256))
+    assert olmoe.plan_gemms(480) == ((1, 64), (1, 64))
+    assert olmoe.plan_gemms(481) == ((2, 256), (2, 256))
 
 
 def test_large_batch_32bit_offset_limit():
