@@ -176,10 +176,12 @@ def test_layer_mixed_tiers_small():
 def test_token_group_sizes(T):
     """All T tokens routed to experts 2 and 5 (large bias): one group of T rows
     per expert, T = 1..128 (the token-group sizes the ExactMoE kernel tests
-    cover, section 5.3), across the tile boundaries of both GEMMs; past 32
-    routes per expert the large-batch kernel runs, whose partial tiles skip
-    the 16-row blocks and weight loads past the group (129..257: both halves
-    of the 256-row tile, a full tile, a full tile plus one row)."""
+    cover, section 5.3), across the tile boundaries of both GEMMs.  The plan
+    sees T / 4 routes per expert on average (8 experts, top-2) and few decode
+    waves: 8-row tiles up to T = 16, split-K 16-row tiles up to T = 112, and
+    past that the large-batch kernel, whose partial tiles skip the 16-row
+    blocks and weight loads past the group (129..257: both halves of the
+    256-row tile, a full tile, a full tile plus one row)."""
     cfg = dataclasses.replace(inputs.get_config(1), max_tokens=300)
     b = np.zeros(8, np.float32)
     b[[2, 5]] = 100.0
