@@ -160,3 +160,35 @@ def test_wave_routing_survives_other_calls_between_waves():
     layer.set_router_mode(0)                     # drops the waves' routing state
     with pytest.raises(ValueError):
         layer.forward_wave(x, wr, b, y=y, accumulate=True)
+
+
+def test_waves_mixed_plan():
+    """Waves on a forward whose plan pairs the large-batch gate/up GEMM with
+    the decode down GEMM (128 experts, I 512, 64 routes per expert): one wave
+    mapping every expert to itself equals the plain forward bit for bit (the
+    same tiles through the slot map), and two half-waves accumulate to it
+    within fp32 reordering."""
+    import dataclasses
+    import torch
+    import inputs
+    cfg = dataclasses.replace(inputs.get_config(2), inter=512, tokens=(1024,), max_tokens=1024)
+    st = Setup(2, T=1024, cfg=cfg)
+    layer = st.gpu_layer()
+    assert layer.plan_gemms(st.T) == ((2, 256), (1, 64))
+    x, wr, b = st.dev_inputs()
+    y = layer.forward(x, wr, b, out_dtype=torch.float32)
+    layer.set_slots(0, layer.handles)
+    layer.set_slot_map(list(range(st.E)))
+    y_one = layer.forward_wave(x, wr, b, out_dtype=torch.float32)
+    half = st.E // 2
+    y_acc = torch.zeros_like(y)
+    layer.set_slot_map([e if e < half else -1 for e in range(st.E)])
+    layer.forward_wave(x, wr, b, y=y_acc)
+    layer.set_slot_map([e if e >= half else -1 for e in range(st.E)])
+    layer.forward_wave(x, wr, b, y=y_acc, accumulate=True)
+    torch.cuda.synchronize()
+    rms = float(torch.sqrt(torch.mean(y.double() ** 2)))
+    gap = float(torch.max(torch.abs(y_acc.double() - y.double()))) / rms
+    log(f"mixed-plan waves: one wave bitwise {torch.equal(y_one, y)}; two waves vs forward {gap:.2e}")
+    assert torch.equal(y_one.view(torch.int32), y.view(torch.int32))
+    assert gap <= 1e-5
