@@ -454,6 +454,13 @@ __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, co
   (void)rw;   // used only when FULL is false
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
+  // FULL false (a tile of at most 128 rows): wave row 1 holds no real row, so
+  // it runs a loop of its own that only stages (its share of the weights and
+  // of the activation DMA, whose rows past the tile repeat real ones) and
+  // skips the operand reads and MFMAs.  The skip is per wave and loop: a
+  // per-64-row-half variant, and one that also skipped the DMA of empty rows,
+  // spilled 60-158 VGPRs.
+  const bool active = FULL || rw.any(wm);               // wave-uniform
   const int K = a.K, G = K / kGroup, KC = K / PBK;
   constexpr int kWaitVmcntB = wait_vmcnt(staged_loads<TIER>());
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(blob, payload_bytes<TIER>(a.N, K));
@@ -504,8 +511,7 @@ __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, co
     load_b_chunk<TIER>(raw, rsrc, bvoff, soff, kc & 1, ks_own);
     if constexpr (TIER == MOE_TIER_INT4) raw.scale = buffer_load_u16(rsrc, svoff, soff + 4096u);
   };
-  auto dma_a = [&](int kc, int buf) {
-    if (!FULL && !rw.dma(wave)) return;
+  auto dma_a = [&](int kc, int buf) {   // every wave (a conditional DMA here spills)
     lds_u8* dst = As(buf) + 4 * wave * 1024;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -521,25 +527,17 @@ __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, co
     const lds_u8* Aw = As(buf) + 8 * wm * 2048 + aread[ks];
     const lds_u8* Bw = Bs(buf) + (2 * 4 * wn + ks) * kFragBytes + 16 * lane;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (FULL || rw.blk(wm, 4 * h)) {
-#pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i)
-          fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
-      }
+    for (int i = 0; i < 8; ++i)
+      fa[ks][i] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Aw + i * 2048));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       fb[ks][j] = __builtin_bit_cast(f16x8_t, (v4u32)*reinterpret_cast<const lds_u4*>(Bw + 2 * j * kFragBytes));
   };
   auto mfma_block = [&](int ks) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (FULL || rw.blk(wm, 4 * h)) {
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
-      }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(fa[ks][i], fb[ks][j], acc[i][j]);
   };
 
   // One chunk: its successor's activations stream into the other buffer by
@@ -562,15 +560,33 @@ __device__ __forceinline__ void prefill_mainloop_staged(const PrefillArgs& a, co
     __builtin_amdgcn_s_waitcnt(kWaitVmcntB);   // the successor's DMA is done; the weights ahead may fly
     __syncthreads();
   };
+  // the same step for a wave row without real rows: its share of the
+  // activation DMA (none past the rows) and of the weight staging, and the
+  // same barriers
+  auto step_stage_only = [&](int kc, BStage<TIER>& next_raw, BStage<TIER>& ahead_raw) {
+    const int buf = kc & 1;
+    dma_a(min(kc + 1, KC - 1), buf ^ 1);
+    load_b(min(kc + 2, KC - 1), ahead_raw);
+    store_b(buf ^ 1, next_raw);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntB);
+    __syncthreads();
+  };
   load_b(0, braw0);
   dma_a(0, 0);
   load_b(1, braw1);
   store_b(0, braw0);
   __builtin_amdgcn_s_waitcnt(kWaitVmcntB);
   __syncthreads();
-  for (int kc = 0; kc < KC; kc += 2) {
-    step(kc, braw1, braw0);
-    step(kc + 1, braw0, braw1);
+  if (FULL || active) {
+    for (int kc = 0; kc < KC; kc += 2) {
+      step(kc, braw1, braw0);
+      step(kc + 1, braw0, braw1);
+    }
+  } else {
+    for (int kc = 0; kc < KC; kc += 2) {
+      step_stage_only(kc, braw1, braw0);
+      step_stage_only(kc + 1, braw0, braw1);
+    }
   }
 }
 
@@ -600,8 +616,8 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // row-aware main loop for partial int4 tiles, skipping 32-row pairs of
-  // 16-row blocks past the tile's rows (the staged tiers always run the full
-  // tile: their row-aware variant spills 96-158 VGPRs)
+  // 16-row blocks past the tile's rows; the staged tiers skip only a whole
+  // empty wave row (tiles of at most 128 rows)
   const RowWork rw{te.rows};
   const bool full = te.rows >= PBM;          // tile-uniform
   if constexpr (TIER == MOE_TIER_INT4) {
@@ -613,8 +629,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, const TileEnt
     } else {
       prefill_mainloop_direct<GATE_UP, false, false>(a, blob, arow, n_block, plds, acc, rw);
     }
-  } else {
+  } else if (full || te.rows > kSplitKMaxRows) {
     prefill_mainloop_staged<TIER, GATE_UP, true>(a, blob, arow, n_block, plds, acc, rw);
+  } else {
+    prefill_mainloop_staged<TIER, GATE_UP, false>(a, blob, arow, n_block, plds, acc, rw);
   }
   const int col0 = n_block + 64 * wn;      // first packed column of this wave (one quad)
   if constexpr (GATE_UP) {
