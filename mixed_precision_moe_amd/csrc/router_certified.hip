@@ -155,10 +155,16 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
   }
 }
 
-// 2.-4. One wave per token.  cid / cb / zc (LDS) hold the candidates' ids,
-// biases and canonical logits, numbered in increasing expert id.
-template <int PER>
-__global__ __launch_bounds__(64) void router_select_kernel(
+// 2.-4. One block of W waves per token.  Wave 0 finds the candidates; cid /
+// cb / zc (LDS) hold their ids, biases and canonical logits, numbered in
+// increasing expert id.  Every half-wave of the block then recomputes its
+// share of the candidates, and wave 0 selects.  With few tokens, several waves
+// per token run the candidates' memory round trips side by side (Qwen3-80B
+// shape, T = 1024: routing 47.9 -> 42.5 us with four); with many, one wave per
+// token already fills the GPU and more only add barriers (T = 4096: 95.4 ->
+// 102.8 us with four).
+template <int PER, int W>
+__global__ __launch_bounds__(64 * W) void router_select_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ vpart, const float* __restrict__ xpart,
     const float* __restrict__ wpart, int T, int H, int E, int S, int k, float cgam,
@@ -166,111 +172,118 @@ __global__ __launch_bounds__(64) void router_select_kernel(
   __shared__ int cid[64 * PER];
   __shared__ float cb[64 * PER];
   __shared__ float zc[64 * PER];
+  __shared__ int ncand;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x;
-  if (t >= T) return;
-  // sums of the S partials: each split's loads for all of the lane's experts
-  // are issued together
-  const int per = (E + 63) / 64;
-  float val[PER], eps[PER], bb[PER], w2[PER];
+  if (t >= T) return;   // block-uniform
+  if (threadIdx.x < 64) {   // wave 0: the candidates
+    // sums of the S partials: each split's loads for all of the lane's experts
+    // are issued together
+    const int per = (E + 63) / 64;
+    float val[PER], eps[PER], bb[PER], w2[PER];
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    val[m] = 0.0f;
-    w2[m] = 0.0f;
-  }
-  float xn2 = 0.0f;
-  for (int z = 0; z < S; ++z) {
-    xn2 += xpart[(size_t)z * T + t];
-    const float* vz = vpart + ((size_t)z * T + t) * E;
-    const float* wz = wpart + (size_t)z * E;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {   // clamped, branch-free loads
-      const int e = min(lane + 64 * m, E - 1);
-      val[m] += vz[e];
-      w2[m] += wz[e];
+    for (int m = 0; m < PER; ++m) {
+      val[m] = 0.0f;
+      w2[m] = 0.0f;
     }
-  }
-  const float nx = sqrtf(xn2);
-  float braw[PER];
-  if (bias) {   // wave-uniform; clamped loads issued together
+    float xn2 = 0.0f;
+    for (int z = 0; z < S; ++z) {
+      xn2 += xpart[(size_t)z * T + t];
+      const float* vz = vpart + ((size_t)z * T + t) * E;
+      const float* wz = wpart + (size_t)z * E;
 #pragma unroll
-    for (int m = 0; m < PER; ++m) braw[m] = bias[min(lane + 64 * m, E - 1)];
-  } else {
+      for (int m = 0; m < PER; ++m) {   // clamped, branch-free loads
+        const int e = min(lane + 64 * m, E - 1);
+        val[m] += vz[e];
+        w2[m] += wz[e];
+      }
+    }
+    const float nx = sqrtf(xn2);
+    float braw[PER];
+    if (bias) {   // wave-uniform; clamped loads issued together
 #pragma unroll
-    for (int m = 0; m < PER; ++m) braw[m] = 0.0f;
-  }
+      for (int m = 0; m < PER; ++m) braw[m] = bias[min(lane + 64 * m, E - 1)];
+    } else {
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int e = lane + 64 * m;
-    const bool ok = m < per && e < E;
-    const float b = ok ? braw[m] : 0.0f;
-    const float v = val[m] + b;
-    bb[m] = b;
-    val[m] = ok ? v : -INFINITY;
-    eps[m] = ok ? cgam * nx * sqrtf(w2[m]) + 0x1p-22f * (fabsf(v) + fabsf(b)) + 1e-30f : 0.0f;
-  }
-  // theta: the k-th largest v - eps (one entry taken per round)
-  uint32_t taken = 0;
-  float theta = -INFINITY;
-#pragma unroll
-  for (int jj = 0; jj < kMaxTopK; ++jj) {
-    if (jj >= k) break;
-    float bv = -INFINITY;
-    int bm = -1;
+      for (int m = 0; m < PER; ++m) braw[m] = 0.0f;
+    }
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
       const int e = lane + 64 * m;
-      const float lo = val[m] - eps[m];
-      if (m < per && e < E && !((taken >> m) & 1u) && (bm < 0 || lo > bv)) {
-        bv = lo;
-        bm = m;
-      }
+      const bool ok = m < per && e < E;
+      const float b = ok ? braw[m] : 0.0f;
+      const float v = val[m] + b;
+      bb[m] = b;
+      val[m] = ok ? v : -INFINITY;
+      eps[m] = ok ? cgam * nx * sqrtf(w2[m]) + 0x1p-22f * (fabsf(v) + fabsf(b)) + 1e-30f : 0.0f;
     }
-    const float wmax = __ockl_wfred_max_f32(bv);
-    const uint64_t mask = __ballot(bm >= 0 && bv == wmax);
-    // mask is 0 only with NaN logits (out of domain; then every expert
-    // becomes a candidate below)
-    if (lane == __ffsll((unsigned long long)mask) - 1) taken |= 1u << bm;
-    if (mask) theta = wmax;
-  }
-  // candidates: v + eps >= theta, numbered in increasing expert id
-  int c = 0;
+    // theta: the k-th largest v - eps (one entry taken per round)
+    uint32_t taken = 0;
+    float theta = -INFINITY;
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int e = lane + 64 * m;
-    const bool cand = m < per && e < E && val[m] + eps[m] >= theta;
-    const uint64_t mask = __ballot(cand);
-    const int at = c + __popcll(mask & ((1ull << lane) - 1ull));
-    if (cand) {
-      cid[at] = e;
-      cb[at] = bb[m];
+    for (int jj = 0; jj < kMaxTopK; ++jj) {
+      if (jj >= k) break;
+      float bv = -INFINITY;
+      int bm = -1;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const int e = lane + 64 * m;
+        const float lo = val[m] - eps[m];
+        if (m < per && e < E && !((taken >> m) & 1u) && (bm < 0 || lo > bv)) {
+          bv = lo;
+          bm = m;
+        }
+      }
+      const float wmax = __ockl_wfred_max_f32(bv);
+      const uint64_t mask = __ballot(bm >= 0 && bv == wmax);
+      // mask is 0 only with NaN logits (out of domain; then every expert
+      // becomes a candidate below)
+      if (lane == __ffsll((unsigned long long)mask) - 1) taken |= 1u << bm;
+      if (mask) theta = wmax;
     }
-    c += __popcll(mask);
-  }
-  if (c < k) {   // only with NaN logits (out of domain): every expert is a candidate
-    for (int i = lane; i < E; i += 64) {
-      cid[i] = i;
-      cb[i] = bias ? bias[i] : 0.0f;
+    // candidates: v + eps >= theta, numbered in increasing expert id
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int e = lane + 64 * m;
+      const bool cand = m < per && e < E && val[m] + eps[m] >= theta;
+      const uint64_t mask = __ballot(cand);
+      const int at = c + __popcll(mask & ((1ull << lane) - 1ull));
+      if (cand) {
+        cid[at] = e;
+        cb[at] = bb[m];
+      }
+      c += __popcll(mask);
     }
-    c = E;
-  }
+    if (c < k) {   // only with NaN logits (out of domain): every expert is a candidate
+      for (int i = lane; i < E; i += 64) {
+        cid[i] = i;
+        cb[i] = bias ? bias[i] : 0.0f;
+      }
+      c = E;
+    }
+    if (lane == 0) ncand = c;
+  }   // wave 0
   __syncthreads();
-  // canonical logits of the candidates: half-wave h takes candidates 2p + h
-  // (p = 0, 1, ...); lane j of the half is chain j.  The half streams its
-  // slabs (p outer, slab inner) in batches of four, two batches in flight.
-  const int j = lane & 31, hw = lane >> 5;
-  const int ns = H >> 8, Q = ((c + 1) >> 1) * ns;
+  const int c = ncand;
+  // canonical logits of the candidates: half-wave h (of NH) takes candidates
+  // NH p + h (p = 0, 1, ...); lane j of the half is chain j.  The half
+  // streams its slabs (p outer, slab inner) in batches of four, two batches
+  // in flight.
+  constexpr int NH = 2 * W;
+  const int j = lane & 31, hw = threadIdx.x >> 5;
+  const int ns = H >> 8, Q = ((c + NH - 1) / NH) * ns;
   const uint16_t* xrow = x + (size_t)t * H + 8 * j;
   int ip = 0, is = 0;   // issue cursor (round, slab)
   auto issue = [&](u32x4 (&wv)[4], u32x4 (&xv)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int e = cid[min(2 * ip + hw, c - 1)];
+      const int e = cid[min(NH * ip + hw, c - 1)];
       wv[u] = load_u32x4(wr + (size_t)e * H + 256 * is + 8 * j);
       xv[u] = load_u32x4(xrow + 256 * is);
       if (++is == ns) {
         is = 0;
-        ip = min(ip + 1, (c - 1) >> 1);   // past the end: repeat the last round's rows
+        ip = min(ip + 1, (c - 1) / NH);   // past the end: repeat the last round's rows
       }
     }
   };
@@ -290,7 +303,7 @@ __global__ __launch_bounds__(64) void router_select_kernel(
         if (++cs == ns) {                          // wave-uniform
 #pragma unroll
           for (int sh = 16; sh >= 1; sh >>= 1) acc = acc + __shfl_down(acc, sh, 32);
-          const int jc = 2 * cp + hw;
+          const int jc = NH * cp + hw;
           if (j == 0 && jc < c) zc[jc] = acc + cb[jc];
           acc = 0.0f;
           cs = 0;
@@ -309,6 +322,7 @@ __global__ __launch_bounds__(64) void router_select_kernel(
     issue(wb, xb);
   }
   __syncthreads();
+  if (W > 1 && threadIdx.x >= 64) return;
   // the canonical top k among the candidates
   float zz[PER];
   int id[PER];
@@ -336,9 +350,20 @@ hipError_t launch_router_certified(const uint16_t* x, const uint16_t* wr, const 
   const double n = (double)H, u = 0x1p-24;
   const float cgam = (float)(2.0 * 2.0 * (n * u / (1.0 - n * u)) * 1.01);
   const int per = (E + 63) / 64;
-#define MOE_SELECT(P)                                                                         \
-  hipLaunchKernelGGL(router_select_kernel<P>, dim3(T), dim3(64), 0, s, x, wr, bias, v, xn2, wn2, \
-                     T, H, E, S, k, cgam, ids, w)
+  // waves per token: about 4096 waves in all, at most four per token
+  const int W = T <= 1024 ? 4 : T <= 2048 ? 2 : 1;
+#define MOE_SELECT1(P, WV)                                                                  \
+  hipLaunchKernelGGL((router_select_kernel<P, WV>), dim3(T), dim3(64 * WV), 0, s, x, wr, bias, \
+                     v, xn2, wn2, T, H, E, S, k, cgam, ids, w)
+#define MOE_SELECT(P)        \
+  do {                       \
+    if (W == 4)              \
+      MOE_SELECT1(P, 4);     \
+    else if (W == 2)         \
+      MOE_SELECT1(P, 2);     \
+    else                     \
+      MOE_SELECT1(P, 1);     \
+  } while (0)
   if (per <= 1)
     MOE_SELECT(1);
   else if (per <= 2)
@@ -350,6 +375,7 @@ hipError_t launch_router_certified(const uint16_t* x, const uint16_t* wr, const 
   else
     MOE_SELECT(kMaxExperts / 64);
 #undef MOE_SELECT
+#undef MOE_SELECT1
   return hipGetLastError();
 }
 
