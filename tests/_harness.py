@@ -23,6 +23,16 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+# Parity margins of the session's layer comparisons: (case, path, error / RMS,
+# tolerance).  tests/conftest.py prints them after the run, so a quiet
+# (-q) log still records each case's margin.
+MARGINS = []
+
+
+def record_margin(case: str, path: int, err: float, tol: float) -> None:
+    MARGINS.append((case, int(path), float(err), float(tol)))
+
+
 def to_dev(a: np.ndarray, dev="cuda:0"):
     import torch
     if a.dtype == np.uint16:

@@ -28,7 +28,8 @@ import pytest
 
 import inputs
 import oracle
-from tests._harness import Setup, bf16_dev_to_np, log, rel_err, tile_boundary_tokens, to_dev
+from tests._harness import (Setup, bf16_dev_to_np, log, record_margin, rel_err,
+                            tile_boundary_tokens, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +67,9 @@ def _run(st: Setup, layer=None, subset=None, keep=True, runs=2):
     got16 = oracle.bf16_bits_to_f32(y16n if subset is None else y16n[subset])
     log(f"  path {path}: max|err|/rms f32 = {err:.3e} (tol {TOL[path]:.1e})   "
         f"bf16 output = {rel_err(got16, y_ref):.3e}")
+    record_margin(f"H{st.H} E{st.E} k{st.k} I{st.I} T={st.T} "
+                  f"tiers={np.bincount(st.tiers, minlength=3).tolist()} tiles={bm13}/{bm2}"
+                  + ("" if subset is None else f" ({len(subset)} tokens)"), path, err, TOL[path])
     assert err <= TOL[path]
     return layer, y32n
 
