@@ -267,7 +267,8 @@ size_t moe_workspace_size(moe_layer_t layer, int32_t T);
  *   logits   [T, E] fp32 or NULL: z, summed in the fixed order
  *            chain j = sum over slabs i, then r = 0..7, of x[256i+8j+r]*wr[..]
  *            (32 chains), folded pairwise (j += j+s for s = 16,8,4,2,1), plus b.
- *   expert_offsets [E+1] int32: exclusive prefix sum of routes per expert.
+ *   expert_offsets [E+1] int32 (4-byte aligned): exclusive prefix sum of
+ *                  routes per expert.
  *   sorted_routes  [T*k] int32: route ids r = t*k + j grouped by expert, each
  *                  group in increasing token order.
  *   route_pos      [T*k] int32: position of route r in sorted_routes.
@@ -280,7 +281,9 @@ size_t moe_workspace_size(moe_layer_t layer, int32_t T);
  * at most 256 KiB of router weights, one launch computes each token's
  * logits in this fixed order on chip and takes its top k there (again the
  * same results).
- * T may be 0 (then only expert_offsets is written, all zero). */
+ * x and wr must be 16-byte aligned, ws 256-byte aligned.
+ * T may be 0 (then only expert_offsets is written, all zero, by a kernel:
+ * the call records no memset, so it can be captured in a HIP graph). */
 int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr,
               const float* bias, int32_t T, int32_t* topk_ids, float* topk_w,
               float* logits, int32_t* expert_offsets, int32_t* sorted_routes,

@@ -644,10 +644,13 @@ int moe_route(moe_layer_t layer, const uint16_t* x, const uint16_t* wr, const fl
   if (rc) return rc;
   if (!expert_offsets || (T > 0 && (!topk_ids || !topk_w || !sorted_routes || !route_pos)))
     return set_error(MOE_EINVAL, "null output pointer");
+  if (!aligned(expert_offsets, 4)) return set_error(MOE_EINVAL, "expert_offsets must be 4-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // no tokens: all offsets are zero (a fill kernel, not a memset node, so a
+  // captured graph replays it correctly)
   if (T == 0)
-    return check_hip(hipMemsetAsync(expert_offsets, 0, sizeof(int32_t) * (L->E + 1), s),
-                     "hipMemsetAsync(offsets)");
+    return check_hip(launch_fill_zero(expert_offsets, sizeof(int32_t) * (L->E + 1), s),
+                     "fill(offsets)");
   const Stages st{L, s, false};
   const hipError_t e = enqueue_route(*L, WaveMap{nullptr, nullptr}, Hotness{nullptr, 1.0f}, p, gp,
                                      x, wr, bias, T, logits, topk_ids, topk_w,

@@ -229,6 +229,13 @@ def test_zero_tokens():
     y = layer.forward(x, wr, None)
     torch.cuda.synchronize()
     assert y.shape == (0, st.H)
+    # routing no tokens writes only the expert offsets, all zero (a fill
+    # kernel); the block the allocator hands out held sevens just before
+    junk = torch.full((st.E + 1,), 7, dtype=torch.int32, device="cuda:0")
+    del junk
+    r = layer.route(x, wr, None)
+    torch.cuda.synchronize()
+    assert r["offsets"].cpu().tolist() == [0] * (st.E + 1)
 
 
 def test_workspace_too_small():
