@@ -303,14 +303,16 @@ __device__ __forceinline__ TileSource tile_source(const DevHandle* table, WaveMa
   return TileSource{wave.slot_map ? wave.slots[active ? slot : 0] : table[e], active};
 }
 
-// Large-batch tile tables (bm >= kSortTilesMinBm) list every expert's full
-// tiles first (expert order), then the partial tiles by row count,
-// descending: the large-batch GEMMs process tiles in table order, so the
-// cheapest tiles (row-aware partial tiles) fill the GPU's last round.  The
-// order comes from a counting sort over the bm row counts (LDS histogram,
-// block scan, atomic placement); partial tiles with equal row counts may
-// land in either order, which changes no result (every tile writes only its
-// own rows).  hist[] is LDS scratch of kMaxTileRows ints.
+// Tile tables of bm >= kSortTilesMinBm rows are ordered by cost, since the
+// GEMMs process tiles in table order and the cheapest should fill the GPU's
+// last round.  Large-batch tables (256 rows) list every expert's full tiles
+// first (expert order), then the partial tiles by row count, descending
+// (row-aware partial tiles are cheaper); 64-row decode tables put the bf16
+// tiles before the others, each part in that same order (see place_tiles).
+// The orders come from counting sorts (LDS histogram, block scan, atomic
+// placement); tiles with equal keys may land in either order, which changes
+// no result (every tile writes only its own rows).  hist[] is LDS scratch of
+// kMaxTileRows ints.
 constexpr int kSortTilesMinBm = 64;
 constexpr int kMaxTileRows = 256;
 
