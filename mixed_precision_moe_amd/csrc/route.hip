@@ -384,6 +384,10 @@ __device__ __forceinline__ void place_tiles(const TileSource& src, const int* of
     }
     if (rem > 0) put(atomicAdd(&hist[kpart], 1), nfull, rem);
     count = tot;
+    // an expert spanning six or more 64-row tiles (most of a group of
+    // kDecodeTileGroup = 8) turns on the decode GEMMs' XCD grouping of
+    // consecutive tiles; an expert's full tiles are consecutive here
+    many = __syncthreads_or(nfull + (rem > 0 ? 1 : 0) >= 6) ? 1 : 0;
   } else {
     const int nfull = ce / bm, rem = ce - nfull * bm;
     int nf = 0;
